@@ -1,0 +1,153 @@
+/*
+ * puro_fp8.h -- blockwise E4M3 FP8 quantise-and-GEMM for gfx950 (MI355X).
+ *
+ * The operation.  The Puro-2B-Base model card (friendli.ai and alphaneural.io
+ * copies; training-setup paragraph under the Phase 1 / Phase 2 table) states
+ * that the main Transformer linear-layer GEMMs of the recipe run in blockwise
+ * E4M3 FP8, while numerically sensitive operations, master weights and
+ * optimizer states stay in BF16 or FP32.  The Puro-2B technical report (part
+ * 7/7, related-work paragraph on low-precision training) places this in the
+ * DeepSeek-V3 line of FP8 mixed-precision training and cites the FP8-formats
+ * paper, whose E4M3 encoding is used here (OCP E4M3FN: bias 7, largest finite
+ * 448, S.1111.111 = NaN, no infinities).  The pages give neither block shapes
+ * nor a scale rule; this library uses:
+ *   - activations and gradients: 1x128 blocks along the contraction dimension;
+ *   - weights: 128x128 tiles;
+ *   - per block: s = fl32(amax / 448), q = E4M3(fl32(x / s)) with round to
+ *     nearest even and saturation at +-448; a block whose s is 0 stores s = 0
+ *     and codes 0x00 / 0x80 (by sign);
+ *   - GEMM: for every 128-wide K block, the FP8 x FP8 block dot product is
+ *     formed on the matrix cores and promoted into FP32 accumulators as
+ *     acc += (sA * sB) * partial; the result is stored as FP32 or BF16 (RNE).
+ * Extents need not be multiples of 128: the last block along an extent then
+ * holds the remaining elements, and its scale is taken over those only.
+ *
+ * Conventions shared by every call.
+ *   - All tensors are row-major.  Every tensor pointer (x, w, q, A, B, C) is a
+ *     DEVICE pointer owned by the caller and must be 16-byte aligned; every
+ *     leading dimension (ld*) is in elements, must be >= the row length and a
+ *     multiple of 16.  Scale pointers are DEVICE pointers to dense FP32 arrays,
+ *     4-byte aligned.  A pointer may be NULL only when its tensor is empty.
+ *   - Arguments are validated on the host, synchronously, before anything is
+ *     enqueued; a failed validation returns an error and enqueues nothing.
+ *   - On success the work is enqueued on `stream` (NULL = the null stream) and
+ *     the call returns without synchronising.  Results are defined once the
+ *     stream reaches that point.
+ *   - The library allocates nothing and keeps no per-call state; calls are
+ *     reentrant.  No C++ exception crosses this interface.
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ *   - Outputs must not overlap inputs.
+ */
+#ifndef PURO_FP8_H
+#define PURO_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PURO_OK = 0,
+    PURO_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    PURO_ERR_SHAPE = 2,     /* negative extent, or leading dimension < row length */
+    PURO_ERR_ALIGN = 3,     /* misaligned pointer or leading dimension             */
+    PURO_ERR_ENUM = 4,      /* unknown dtype / layout / granularity value          */
+    PURO_ERR_WORKSPACE = 5, /* workspace missing or smaller than required          */
+    PURO_ERR_HIP = 6,       /* the HIP runtime reported an error at launch         */
+    PURO_ERR_INTERNAL = 7   /* unexpected internal failure                         */
+} puro_status_t;
+
+typedef enum { PURO_F32 = 0, PURO_BF16 = 1 } puro_dtype_t;
+
+/* Operand orientation of puro_fp8_gemm; C is always [M][N], contraction over K. */
+typedef enum {
+    PURO_NT = 0, /* A [M][K], B [N][K]  -- forward Y = X W^T; weight gradient on token-transposed copies */
+    PURO_NN = 1, /* A [M][K], B [K][N]  -- data gradient dX = dY W with the forward's quantised W        */
+    PURO_TN = 2  /* A [K][M], B [K][N]  -- weight gradient dW = dY^T X on untransposed token-blocked copies */
+} puro_layout_t;
+
+/* Block shape of B's scales; A's scales are always 1x128 along K. */
+typedef enum { PURO_SCALE_1x128 = 0, PURO_SCALE_128x128 = 1 } puro_bscale_t;
+
+/*
+ * Activation / gradient quantiser (1x128 along each row).
+ *   x   [rows][cols], FP32 or BF16 (xdt), row stride ldx
+ *   q   [rows][cols] E4M3 codes, row stride ldq
+ *   s   [rows][ceil(cols/128)] FP32, dense
+ * Block (r, b) is x[r][128b .. min(cols, 128b+128)).
+ * Used for the forward input X of every linear layer and for the incoming
+ * gradient dY of the data-gradient GEMM (blocked along the output features).
+ */
+puro_status_t puro_fp8_quant_act(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *q, int64_t ldq, float *s,
+                                 hipStream_t stream);
+
+/*
+ * Weight quantiser (128x128 tiles).
+ *   w   [rows][cols], FP32 or BF16 (wdt) master weight, row stride ldw
+ *   q   [rows][cols] E4M3 codes, row stride ldq
+ *   s   [ceil(rows/128)][ceil(cols/128)] FP32, dense
+ * One scale per tile; the same codes and scales serve the forward GEMM (NT,
+ * B = W [N_out][K_in]) and the data-gradient GEMM (NN, B = W read as [K][N]).
+ */
+puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,
+                                    int64_t ldw, uint8_t *q, int64_t ldq, float *s,
+                                    hipStream_t stream);
+
+/*
+ * Token-dimension quantiser for the weight-gradient GEMM: blocks are 128
+ * consecutive tokens of one column of x [tokens][cols] (FP32 or BF16, stride ldx).
+ *   transpose_out = 1: q [cols][tokens] (stride ldq), s [cols][ceil(tokens/128)]
+ *                      -- operands of an NT weight-gradient GEMM
+ *   transpose_out = 0: q [tokens][cols] (stride ldq), s [ceil(tokens/128)][cols]
+ *                      -- operands of a TN weight-gradient GEMM
+ * Both modes produce the same codes and scales, laid out differently.
+ * Any other transpose_out value returns PURO_ERR_ENUM.
+ */
+puro_status_t puro_fp8_quant_transpose(const void *x, puro_dtype_t xdt, int64_t tokens,
+                                       int64_t cols, int64_t ldx, int transpose_out, uint8_t *q,
+                                       int64_t ldq, float *s, hipStream_t stream);
+
+/*
+ * Workspace bytes puro_fp8_gemm needs for this problem (0 = none).  Returns 0
+ * for invalid arguments as well; puro_fp8_gemm reports those.
+ */
+size_t puro_fp8_gemm_workspace_size(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                                    puro_bscale_t bgran);
+
+/*
+ * Blockwise-scaled FP8 GEMM:
+ *   C[m][n] = sum_kb sA(m,kb) * sB(n,kb) * sum_{k in block kb} a(m,k) b(k,n)
+ * with a, b the E4M3 values of A and B, kb over the ceil(K/128) blocks of K.
+ * Storage (KB = ceil(K/128), NB = ceil(N/128)); scales are dense and indexed
+ * in the operand's storage orientation:
+ *   layout   A        sA         B        sB (1x128)  sB (128x128)
+ *   NT       [M][K]   [M][KB]    [N][K]   [N][KB]     [NB][KB]
+ *   NN       [M][K]   [M][KB]    [K][N]   [KB][N]     [KB][NB]
+ *   TN       [K][M]   [KB][M]    [K][N]   [KB][N]     [KB][NB]
+ * C [M][N] (row stride ldc) is written as FP32 or BF16 (cdt, round to nearest
+ * even); it is overwritten, not accumulated into.  K = 0 writes zeros.
+ * workspace may be NULL when puro_fp8_gemm_workspace_size returns 0;
+ * otherwise it must hold at least that many bytes (device memory, 256-byte
+ * aligned) and must not be used by other work in flight on other streams.
+ */
+puro_status_t puro_fp8_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                            const uint8_t *A, int64_t lda, const float *sA, const uint8_t *B,
+                            int64_t ldb, const float *sB, puro_bscale_t bgran, void *C,
+                            puro_dtype_t cdt, int64_t ldc, void *workspace, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *puro_status_string(puro_status_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int puro_fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PURO_FP8_H */
