@@ -1,0 +1,282 @@
+"""Benchmark: blockwise-FP8 linear-layer GEMMs of the Qwen3-1.7B stack on one MI355X.
+
+One step = one micro-batch (2 x 4,096 = 8,192 tokens) through the linear
+layers of all 28 Transformer layers: the seven unfused projections
+(q, k, v, o, gate, up, down) in forward (Y = X W^T), data gradient
+(dX = dY W) and weight gradient (dW = dY^T X), with every quantiser
+(activations 1x128, weights 128x128, gradients 1x128, token-dimension copies
+for the weight gradient) inside the timed region.  Shapes come from the
+Puro-2B-Base model card (Qwen3-1.7B configuration: hidden 2,048, FFN 6,144,
+16 / 8 heads, 28 layers; sequence length 4,096, micro-batch 2).
+
+Inputs are seeded synthetic tensors already resident in HBM: activations
+BF16 N(0,1), gradients BF16 N(0,1e-3), FP32 master weights N(0,0.02), fresh
+per layer.  Output: one JSON line (see the end of main()).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "blockwise-FP8 GEMM TFLOP/s (fwd+dgrad+wgrad), Qwen3-1.7B shapes; % FP8 peak"
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (published)
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Plan:
+    """Pre-marshalled C-ABI calls of one step (pointers fixed, buffers preallocated)."""
+
+    def __init__(self):
+        self.calls = []   # (fn, args, kind, name, flops, bytes)
+
+    def add(self, fn, args, kind, name, flops=0.0, nbytes=0.0):
+        self.calls.append((fn, args, kind, name, flops, nbytes))
+
+    def run(self):
+        for fn, args, _, _, _, _ in self.calls:
+            st = fn(*args)
+            if st:
+                raise RuntimeError("C-ABI call failed with status %d" % st)
+
+
+def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
+    """Allocate the stack's inputs (seeded, on the GPU) and outputs; return (plan, keepalive)."""
+    import synth
+    L = pf.lib()
+    vp = ctypes.c_void_p
+    keep = []
+    plan = Plan()
+    bf16, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+
+    def P(t):
+        return vp(t.data_ptr())
+
+    def nb(n):
+        return (n + 127) // 128
+
+    # Reused per-layer work buffers, sized for the largest use.
+    max_in = max(k for _, _, k, _ in synth.LAYER_GEMMS)
+    max_out = max(n for _, n, _, _ in synth.LAYER_GEMMS)
+    qx = {name: torch.empty((tokens, c), dtype=u8, device=dev) for name, c in synth.LAYER_INPUTS}
+    sx = {name: torch.empty((tokens, nb(c)), dtype=f32, device=dev) for name, c in synth.LAYER_INPUTS}
+    qxt = {name: torch.empty((c, tokens), dtype=u8, device=dev) for name, c in synth.LAYER_INPUTS}
+    sxt = {name: torch.empty((c, nb(tokens)), dtype=f32, device=dev) for name, c in synth.LAYER_INPUTS}
+    qdy = torch.empty((tokens, max_out), dtype=u8, device=dev)
+    sdy = torch.empty((tokens, nb(max_out)), dtype=f32, device=dev)
+    qdyt = torch.empty((max_out, tokens), dtype=u8, device=dev)
+    sdyt = torch.empty((max_out, nb(tokens)), dtype=f32, device=dev)
+    qw = {g: torch.empty((n, k), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    sw = {g: torch.empty((nb(n), nb(k)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    y = {g: torch.empty((tokens, n), dtype=bf16, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    dx = {g: torch.empty((tokens, k), dtype=bf16, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    dw = {g: torch.empty((n, k), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, y, dx, dw]
+
+    BF16, F32 = pf.PURO_BF16, pf.PURO_F32
+    NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
+    S1, S128 = pf.BGRAN["1x128"], pf.BGRAN["128x128"]
+    T = tokens
+    for layer in range(layers):
+        xs = {name: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
+              for i, (name, c) in enumerate(synth.LAYER_INPUTS)}
+        ws = {g: synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
+              for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
+        dys = {g: synth.device_normal((T, n), 1e-3, synth.seed_of(4, layer, 20 + j), "bf16", dev)
+               for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
+        keep += [xs, ws, dys]
+        # forward: quantise each distinct input once, each weight once, then Y = X W^T
+        for name, c in synth.LAYER_INPUTS:
+            plan.add(L.puro_fp8_quant_act, (P(xs[name]), BF16, T, c, c, P(qx[name]), c, P(sx[name]),
+                                            stream_ptr), "quant_act", "quant_act", 0, T * c * (2 + 1 + 4 / 128))
+        for g, n, k, src in synth.LAYER_GEMMS:
+            plan.add(L.puro_fp8_quant_weight, (P(ws[g]), F32, n, k, k, P(qw[g]), k, P(sw[g]), stream_ptr),
+                     "quant_weight", "quant_weight", 0, n * k * (4 + 1) + nb(n) * nb(k) * 4)
+            plan.add(L.puro_fp8_gemm, (NT, T, n, k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]),
+                                       S128, P(y[g]), BF16, n, None, 0, stream_ptr),
+                     "gemm", "gemm_fwd_NT_128x128_bf16", 2.0 * T * n * k)
+        # data gradient: dX = dY W with the forward's quantised W
+        for g, n, k, src in synth.LAYER_GEMMS:
+            plan.add(L.puro_fp8_quant_act, (P(dys[g]), BF16, T, n, n, P(qdy), n, P(sdy), stream_ptr),
+                     "quant_act", "quant_act", 0, T * n * (2 + 1 + 4 / 128))
+            plan.add(L.puro_fp8_gemm, (NN, T, k, n, P(qdy), n, P(sdy), P(qw[g]), k, P(sw[g]), S128,
+                                       P(dx[g]), BF16, k, None, 0, stream_ptr),
+                     "gemm", "gemm_dgrad_NN_128x128_bf16", 2.0 * T * n * k)
+        # weight gradient: dW = dY^T X on token-blocked copies
+        for name, c in synth.LAYER_INPUTS:
+            plan.add(L.puro_fp8_quant_transpose, (P(xs[name]), BF16, T, c, c, 1, P(qxt[name]), T,
+                                                  P(sxt[name]), stream_ptr),
+                     "quant_transpose", "quant_transpose", 0, T * c * (2 + 1 + 4 / 128))
+        for g, n, k, src in synth.LAYER_GEMMS:
+            plan.add(L.puro_fp8_quant_transpose, (P(dys[g]), BF16, T, n, n, 1, P(qdyt), T, P(sdyt),
+                                                  stream_ptr),
+                     "quant_transpose", "quant_transpose", 0, T * n * (2 + 1 + 4 / 128))
+            plan.add(L.puro_fp8_gemm, (NT, n, k, T, P(qdyt), T, P(sdyt), P(qxt[src]), T, P(sxt[src]),
+                                       S1, P(dw[g]), F32, k, None, 0, stream_ptr),
+                     "gemm", "gemm_wgrad_NT_1x128_f32", 2.0 * T * n * k)
+    return plan, keep
+
+
+def cpu_baseline(rows):
+    """Time the oracle on a bounded sample of one layer of the same workload."""
+    import numpy as np
+    import oracle
+    import synth
+    T = synth.TOKENS
+    rng_layer = 0
+    t_total = 0.0
+    flops = 0.0
+    for j, (g, n, k, src) in enumerate(synth.LAYER_GEMMS):
+        x = synth.normal((rows, k), 1.0, synth.seed_of(4, rng_layer, 100 + j), "bf16")
+        w = synth.normal((n, k), 0.02, synth.seed_of(4, rng_layer, 110 + j))
+        dy = synth.normal((rows, n), 1e-3, synth.seed_of(4, rng_layer, 120 + j), "bf16")
+        xt = synth.normal((T, k), 1.0, synth.seed_of(4, rng_layer, 130 + j), "bf16")
+        dyt = synth.normal((T, rows), 1e-3, synth.seed_of(4, rng_layer, 140 + j), "bf16")
+        t0 = time.perf_counter()
+        qa, sa = oracle.quant_act(x)
+        qw, sw = oracle.quant_weight(w)
+        oracle.gemm("NT", qa, sa, qw, sw, "128x128")                   # rows x n x k
+        qd, sd = oracle.quant_act(dy)
+        oracle.gemm("NN", qd, sd, qw, sw, "128x128")                   # rows x k x n
+        qdt, sdt = oracle.quant_transpose(dyt, True)
+        qxt, sxt = oracle.quant_transpose(xt, True)
+        oracle.gemm("NT", qdt, sdt, qxt, sxt, "1x128")                 # rows x k x T
+        t_total += time.perf_counter() - t0
+        flops += 2.0 * rows * n * k * 2 + 2.0 * rows * k * T
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "one layer, %d rows of each of its 21 GEMMs (fwd/dgrad: %d of 8192 tokens; "
+                      "wgrad: %d output rows, K=8192) with their quantisers; %.1f GFLOP in %.1f s"
+                      % (rows, rows, rows, flops / 1e9, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=28, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-rows", type=int, default=16, help="rows per GEMM in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import blockwise_fp8_gemm_amd as pf
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    tokens = synth.TOKENS
+
+    t0 = time.time()
+    plan, keep = build_stack_plan(pf, torch, dev, args.layers, tokens, sp)
+    torch.cuda.synchronize()
+    log("inputs resident: %d layers, %.1f GB allocated, %d launches per step (%.1fs)"
+        % (args.layers, torch.cuda.memory_allocated() / 1e9, len(plan.calls), time.time() - t0))
+    step_flops = sum(c[4] for c in plan.calls)
+
+    for i in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # Timed region: K whole steps, nothing else on the stream.
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        plan.run()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    log("timed: %.3f ms/step (event), %.3f ms/step (wall)" % (ms_per_step, wall * 1e3 / args.steps))
+
+    # Per-kernel durations: the same K steps again with an event between consecutive launches.
+    nlaunch = len(plan.calls)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nlaunch + 1)]
+    per_kind = {}
+    per_name = {}
+    for i in range(args.steps):
+        evs[0].record(stream)
+        for j, (fn, a, kind, name, fl, nbyt) in enumerate(plan.calls):
+            st = fn(*a)
+            if st:
+                raise RuntimeError("status %d" % st)
+            evs[j + 1].record(stream)
+        torch.cuda.synchronize()
+        for j, (fn, a, kind, name, fl, nbyt) in enumerate(plan.calls):
+            ms = evs[j].elapsed_time(evs[j + 1])
+            k = per_kind.setdefault(kind, [0.0, 0.0, 0.0, 0])
+            k[0] += ms; k[1] += fl; k[2] += nbyt; k[3] += 1
+            n_ = per_name.setdefault(name, [0.0, 0.0, 0.0, 0])
+            n_[0] += ms; n_[1] += fl; n_[2] += nbyt; n_[3] += 1
+    for k, v in sorted(per_kind.items(), key=lambda kv: -kv[1][0]):
+        log("  %-16s %8.3f ms/step  %s" % (k, v[0] / args.steps,
+            ("%.0f TFLOP/s" % (v[1] / v[0] / 1e9)) if v[1] else ("%.0f GB/s" % (v[2] / v[0] / 1e6))))
+    for k, v in sorted(per_name.items(), key=lambda kv: -kv[1][0]):
+        log("  %-28s %8.3f ms/step  calls %d  avg %.1f us  %s" % (
+            k, v[0] / args.steps, v[3] // args.steps, v[0] / v[3] * 1e3,
+            ("%.0f TFLOP/s" % (v[1] / v[0] / 1e9)) if v[1] else ("%.0f GB/s" % (v[2] / v[0] / 1e6))))
+
+    dom_name, dom = max(per_name.items(), key=lambda kv: kv[1][0])
+    gemm_ms = per_kind["gemm"][0] / args.steps
+    if dom[1] > 0:
+        achieved = dom[1] / dom[0] / 1e9            # TFLOP/s
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": dom_name, "avg_launch_us": round(dom[0] / dom[3] * 1e3, 2)}
+    else:
+        achieved = dom[2] / dom[0] / 1e6            # GB/s
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": dom_name, "avg_launch_us": round(dom[0] / dom[3] * 1e3, 2)}
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-1.7B linear stack, %d layers x 7 projections, fwd+dgrad+wgrad, "
+                               "%d tokens (2x4096), quantisers included" % (args.layers, tokens),
+                   "layers": args.layers, "tokens": tokens, "gemms_per_step": 21 * args.layers,
+                   "tflop_per_step": round(step_flops / 1e12, 3)},
+        "pct_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
+        "gemm_only_tflops": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "breakdown_ms": {k: round(v[0] / args.steps, 3) for k, v in per_kind.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a CPU sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+"""Python binding of libpuro_fp8 (blockwise E4M3 FP8 quantise-and-GEMM on gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels behind the
+C-ABI declared in include/puro_fp8.h.  PyTorch supplies device memory and
+the current stream.  There is no CPU fallback: without the built library
+every call raises.
+
+Names mirror the C entry points:
+    puro_fp8_quant_act(x)                 -> (q, s)   1x128 blocks along rows
+    puro_fp8_quant_weight(w)              -> (q, s)   128x128 tiles
+    puro_fp8_quant_transpose(x, t_out)    -> (q, s)   128-token blocks per column
+    puro_fp8_gemm(layout, A, sA, B, sB, bgran, out_dtype) -> C
+    puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
+    puro_status_string(status)
+Tensors are 2-D, row-major (stride(1) == 1), with a row stride that is a
+multiple of 16 elements and 16-byte aligned storage.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpuro_fp8.so")
+
+PURO_OK = 0
+PURO_F32, PURO_BF16 = 0, 1
+LAYOUTS = {"NT": 0, "NN": 1, "TN": 2}
+BGRAN = {"1x128": 0, "128x128": 1}
+
+_lib = None
+
+
+class PuroError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, puro_status_string(status), status))
+
+
+def lib():
+    """Load libpuro_fp8.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libpuro_fp8.so is not built (run blockwise_fp8_gemm_amd/build.py "
+                              "or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        for name in ("puro_fp8_quant_act", "puro_fp8_quant_weight"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
+        L.puro_fp8_quant_transpose.restype = i32
+        L.puro_fp8_quant_transpose.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
+        L.puro_fp8_gemm_workspace_size.restype = ctypes.c_size_t
+        L.puro_fp8_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i32]
+        L.puro_fp8_gemm.restype = i32
+        L.puro_fp8_gemm.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32,
+                                    i64, vp, ctypes.c_size_t, vp]
+        L.puro_status_string.restype = ctypes.c_char_p
+        L.puro_status_string.argtypes = [i32]
+        L.puro_fp8_version.restype = i32
+        L.puro_fp8_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def puro_status_string(status):
+    return lib().puro_status_string(int(status)).decode()
+
+
+def puro_fp8_version():
+    return int(lib().puro_fp8_version())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _ld(t):
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor, got shape %s" % (tuple(t.shape),))
+    if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("expected unit stride along the last dimension")
+    # with at most one row, or no elements, the stride never addresses memory
+    if t.numel() == 0 or t.shape[0] <= 1:
+        return _pad16(t.shape[1])
+    return t.stride(0)
+
+
+def _pad16(n):
+    return (n + 15) // 16 * 16
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return PURO_F32
+    if t.dtype == torch.bfloat16:
+        return PURO_BF16
+    raise TypeError("inputs are float32 or bfloat16, got %s" % t.dtype)
+
+
+def _nblk(n):
+    return (n + 127) // 128
+
+
+def empty_2d(rows, cols, dtype, device):
+    """Uninitialised [rows][cols] tensor whose row stride is a multiple of 16 elements."""
+    ld = _pad16(cols)
+    if ld == cols:
+        return torch.empty((rows, cols), dtype=dtype, device=device)
+    return torch.empty((rows, ld), dtype=dtype, device=device)[:, :cols]
+
+
+def _check(status, what):
+    if status != PURO_OK:
+        raise PuroError(status, what)
+
+
+def _need(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_cuda:
+        raise ValueError("%s: expected %s %s on the GPU, got %s %s" % (
+            name, tuple(shape), dtype, tuple(t.shape), t.dtype))
+
+
+def _need_dense(t, shape, name):
+    _need(t, shape, torch.float32, name)
+    if not t.is_contiguous():
+        raise ValueError("%s: scale arrays must be dense (contiguous)" % name)
+
+
+def puro_fp8_quant_act(x, q=None, s=None, stream=None):
+    """1x128 blocks along each row of x [rows][cols] (float32 / bfloat16)."""
+    rows, cols = x.shape
+    if q is None:
+        q = empty_2d(rows, cols, torch.uint8, x.device)
+    if s is None:
+        s = torch.empty((rows, _nblk(cols)), dtype=torch.float32, device=x.device)
+    _need(q, (rows, cols), torch.uint8, "q")
+    _need_dense(s, (rows, _nblk(cols)), "s")
+    _check(lib().puro_fp8_quant_act(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
+                                    _ptr(s), _stream(stream)), "puro_fp8_quant_act")
+    return q, s
+
+
+def puro_fp8_quant_weight(w, q=None, s=None, stream=None):
+    """128x128 tiles of w [rows][cols] (float32 / bfloat16)."""
+    rows, cols = w.shape
+    if q is None:
+        q = empty_2d(rows, cols, torch.uint8, w.device)
+    if s is None:
+        s = torch.empty((_nblk(rows), _nblk(cols)), dtype=torch.float32, device=w.device)
+    _need(q, (rows, cols), torch.uint8, "q")
+    _need_dense(s, (_nblk(rows), _nblk(cols)), "s")
+    _check(lib().puro_fp8_quant_weight(_ptr(w), _dtype_code(w), rows, cols, _ld(w), _ptr(q),
+                                       _ld(q), _ptr(s), _stream(stream)), "puro_fp8_quant_weight")
+    return q, s
+
+
+def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None):
+    """128-token blocks per column of x [tokens][cols].
+
+    transpose_out=True : q [cols][tokens], s [cols][ceil(tokens/128)]
+    transpose_out=False: q [tokens][cols], s [ceil(tokens/128)][cols]
+    """
+    tokens, cols = x.shape
+    qshape = (cols, tokens) if transpose_out else (tokens, cols)
+    sshape = (cols, _nblk(tokens)) if transpose_out else (_nblk(tokens), cols)
+    if q is None:
+        q = empty_2d(qshape[0], qshape[1], torch.uint8, x.device)
+    if s is None:
+        s = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    _need(q, qshape, torch.uint8, "q")
+    _need_dense(s, sshape, "s")
+    _check(lib().puro_fp8_quant_transpose(_ptr(x), _dtype_code(x), tokens, cols, _ld(x),
+                                          1 if transpose_out else 0, _ptr(q), _ld(q), _ptr(s),
+                                          _stream(stream)), "puro_fp8_quant_transpose")
+    return q, s
+
+
+def gemm_dims(layout, A, B):
+    """(M, N, K) of a product in the given layout."""
+    if layout == "NT":
+        (M, K), (N, K2) = A.shape, B.shape
+    elif layout == "NN":
+        (M, K), (K2, N) = A.shape, B.shape
+    elif layout == "TN":
+        (K, M), (K2, N) = A.shape, B.shape
+    else:
+        raise ValueError("layout must be NT, NN or TN, got %r" % (layout,))
+    if K != K2:
+        raise ValueError("contraction extents differ: %d vs %d" % (K, K2))
+    return M, N, K
+
+
+def scale_shapes(layout, bgran, M, N, K):
+    """Dense shapes of (sA, sB) for a product."""
+    KB, NB = _nblk(K), _nblk(N)
+    sa = (KB, M) if layout == "TN" else (M, KB)
+    if layout == "NT":
+        sb = (NB, KB) if bgran == "128x128" else (N, KB)
+    else:
+        sb = (KB, NB) if bgran == "128x128" else (KB, N)
+    return sa, sb
+
+
+def puro_fp8_gemm_workspace_size(layout, M, N, K, bgran):
+    return int(lib().puro_fp8_gemm_workspace_size(LAYOUTS[layout], M, N, K, BGRAN[bgran]))
+
+
+def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat16, C=None,
+                  workspace=None, stream=None):
+    """Blockwise-scaled E4M3 GEMM; returns C [M][N] (float32 or bfloat16)."""
+    M, N, K = gemm_dims(layout, A, B)
+    if A.dtype != torch.uint8 or B.dtype != torch.uint8:
+        raise TypeError("A and B hold E4M3 codes (torch.uint8)")
+    sa_shape, sb_shape = scale_shapes(layout, bgran, M, N, K)
+    _need_dense(sA, sa_shape, "sA")
+    _need_dense(sB, sb_shape, "sB")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype is float32 or bfloat16")
+    if C is None:
+        C = empty_2d(M, N, out_dtype, A.device)
+    _need(C, (M, N), out_dtype, "C")
+    need = puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().puro_fp8_gemm(LAYOUTS[layout], M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B),
+                               _ld(B), _ptr(sB), BGRAN[bgran], _ptr(C),
+                               PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32, _ld(C),
+                               _ptr(workspace), ws_bytes, _stream(stream)), "puro_fp8_gemm")
+    return C

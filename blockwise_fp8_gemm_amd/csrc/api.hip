@@ -1,0 +1,217 @@
+// C-ABI entry points: host-side validation, then one enqueue on the caller's
+// stream.  Declarations and the contract of each call are in puro_fp8.h.
+#include "../../include/puro_fp8.h"
+#include "kernels.h"
+
+namespace {
+
+// Largest extent accepted along any dimension (keeps every grid dimension and
+// 64-bit offset computation in range).
+constexpr int64_t kMaxExtent = int64_t(1) << 23;
+
+bool aligned(const void *p, uintptr_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+bool bad_extent(int64_t n)
+{
+    return n < 0 || n > kMaxExtent;
+}
+
+bool bad_ld(int64_t ld, int64_t row_len)
+{
+    return ld < row_len || ld > kMaxExtent;
+}
+
+// Shared checks of the three quantisers.  `elems` is the number of input
+// elements, `nscale` the number of scale entries.
+puro_status_t check_quant(const void *x, int xdt, int64_t rows, int64_t cols, int64_t ldx,
+                          const uint8_t *q, int64_t ldq, int64_t ldq_min, const float *s)
+{
+    if (xdt != PURO_F32 && xdt != PURO_BF16)
+        return PURO_ERR_ENUM;
+    if (bad_extent(rows) || bad_extent(cols) || bad_ld(ldx, cols) || bad_ld(ldq, ldq_min))
+        return PURO_ERR_SHAPE;
+    const bool empty = rows == 0 || cols == 0;
+    if (!empty && (!x || !q || !s))
+        return PURO_ERR_NULL;
+    if (ldx % 16 || ldq % 16)
+        return PURO_ERR_ALIGN;
+    if ((x && !aligned(x, 16)) || (q && !aligned(q, 16)) || (s && !aligned(s, 4)))
+        return PURO_ERR_ALIGN;
+    return PURO_OK;
+}
+
+puro_status_t from_hip(hipError_t e)
+{
+    return e == hipSuccess ? PURO_OK : PURO_ERR_HIP;
+}
+
+} // namespace
+
+extern "C" {
+
+puro_status_t puro_fp8_quant_act(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *q, int64_t ldq, float *s,
+                                 hipStream_t stream)
+{
+    try {
+        puro_status_t st = check_quant(x, xdt, rows, cols, ldx, q, ldq, cols, s);
+        if (st != PURO_OK)
+            return st;
+        if (rows == 0 || cols == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_quant_act(x, xdt == PURO_BF16, rows, cols, ldx, q, ldq, s,
+                                               stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,
+                                    int64_t ldw, uint8_t *q, int64_t ldq, float *s,
+                                    hipStream_t stream)
+{
+    try {
+        puro_status_t st = check_quant(w, wdt, rows, cols, ldw, q, ldq, cols, s);
+        if (st != PURO_OK)
+            return st;
+        if (rows == 0 || cols == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_quant_weight(w, wdt == PURO_BF16, rows, cols, ldw, q, ldq, s,
+                                                  stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+puro_status_t puro_fp8_quant_transpose(const void *x, puro_dtype_t xdt, int64_t tokens,
+                                       int64_t cols, int64_t ldx, int transpose_out, uint8_t *q,
+                                       int64_t ldq, float *s, hipStream_t stream)
+{
+    try {
+        if (transpose_out != 0 && transpose_out != 1)
+            return PURO_ERR_ENUM;
+        puro_status_t st = check_quant(x, xdt, tokens, cols, ldx, q, ldq,
+                                       transpose_out ? tokens : cols, s);
+        if (st != PURO_OK)
+            return st;
+        if (tokens == 0 || cols == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_quant_transpose(x, xdt == PURO_BF16, tokens, cols, ldx,
+                                                     transpose_out == 1, q, ldq, s, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+static puro_status_t check_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                                const uint8_t *A, int64_t lda, const float *sA, const uint8_t *B,
+                                int64_t ldb, const float *sB, puro_bscale_t bgran, const void *C,
+                                puro_dtype_t cdt, int64_t ldc)
+{
+    if (layout != PURO_NT && layout != PURO_NN && layout != PURO_TN)
+        return PURO_ERR_ENUM;
+    if (bgran != PURO_SCALE_1x128 && bgran != PURO_SCALE_128x128)
+        return PURO_ERR_ENUM;
+    if (cdt != PURO_F32 && cdt != PURO_BF16)
+        return PURO_ERR_ENUM;
+    if (bad_extent(M) || bad_extent(N) || bad_extent(K))
+        return PURO_ERR_SHAPE;
+    const int64_t lda_min = layout == PURO_TN ? M : K;
+    const int64_t ldb_min = layout == PURO_NT ? K : N;
+    if (bad_ld(lda, lda_min) || bad_ld(ldb, ldb_min) || bad_ld(ldc, N))
+        return PURO_ERR_SHAPE;
+    const bool a_empty = M == 0 || K == 0, b_empty = N == 0 || K == 0, c_empty = M == 0 || N == 0;
+    if ((!a_empty && (!A || !sA)) || (!b_empty && (!B || !sB)) || (!c_empty && !C))
+        return PURO_ERR_NULL;
+    if (lda % 16 || ldb % 16 || ldc % 16)
+        return PURO_ERR_ALIGN;
+    if ((A && !aligned(A, 16)) || (B && !aligned(B, 16)) || (C && !aligned(C, 16)) ||
+        (sA && !aligned(sA, 4)) || (sB && !aligned(sB, 4)))
+        return PURO_ERR_ALIGN;
+    return PURO_OK;
+}
+
+static puro::GemmProblem make_problem(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                                      const uint8_t *A, int64_t lda, const float *sA,
+                                      const uint8_t *B, int64_t ldb, const float *sB,
+                                      puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc)
+{
+    puro::GemmProblem p;
+    p.layout = (int)layout;
+    p.bgran = (int)bgran;
+    p.c_bf16 = cdt == PURO_BF16;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = A;
+    p.lda = lda;
+    p.sA = sA;
+    p.B = B;
+    p.ldb = ldb;
+    p.sB = sB;
+    p.C = C;
+    p.ldc = ldc;
+    return p;
+}
+
+size_t puro_fp8_gemm_workspace_size(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                                    puro_bscale_t bgran)
+{
+    if (layout != PURO_NT && layout != PURO_NN && layout != PURO_TN)
+        return 0;
+    if (bgran != PURO_SCALE_1x128 && bgran != PURO_SCALE_128x128)
+        return 0;
+    if (bad_extent(M) || bad_extent(N) || bad_extent(K))
+        return 0;
+    puro::GemmProblem p = make_problem(layout, M, N, K, nullptr, 0, nullptr, nullptr, 0, nullptr,
+                                       bgran, nullptr, PURO_F32, 0);
+    return puro::gemm_workspace_bytes(p);
+}
+
+puro_status_t puro_fp8_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                            const uint8_t *A, int64_t lda, const float *sA, const uint8_t *B,
+                            int64_t ldb, const float *sB, puro_bscale_t bgran, void *C,
+                            puro_dtype_t cdt, int64_t ldc, void *workspace, size_t ws_bytes,
+                            hipStream_t stream)
+{
+    try {
+        puro_status_t st = check_gemm(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
+        if (st != PURO_OK)
+            return st;
+        puro::GemmProblem p = make_problem(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt,
+                                           ldc);
+        const size_t need = puro::gemm_workspace_bytes(p);
+        if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
+            return PURO_ERR_WORKSPACE;
+        if (M == 0 || N == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_gemm(p, workspace, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+const char *puro_status_string(puro_status_t status)
+{
+    switch (status) {
+    case PURO_OK: return "success";
+    case PURO_ERR_NULL: return "a required pointer is NULL";
+    case PURO_ERR_SHAPE: return "invalid extent or leading dimension";
+    case PURO_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case PURO_ERR_ENUM: return "unknown enumeration value";
+    case PURO_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case PURO_ERR_HIP: return "HIP runtime error at launch";
+    case PURO_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+int puro_fp8_version(void)
+{
+    return 100;
+}
+
+} // extern "C"

@@ -1,0 +1,72 @@
+// Device helpers shared by the quantiser and GEMM kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace puro {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Four floats -> four E4M3 codes packed little-endian into one dword.
+// v_cvt_pk_fp8_f32 rounds to nearest even into the OCP E4M3 format; it was
+// checked on gfx950 against an integer-only round-to-nearest-even,
+// saturating encoder for every FP32 value with |y| <= 449, which covers every
+// quotient x/s the quantisers form (|x/s| <= 448 * (1 + 2^-23)).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
+{
+    uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)lo, true);
+}
+
+// Code of +-0 by the sign of x: 0x80 for negative values and -0.
+__device__ __forceinline__ uint32_t sign_code(float x)
+{
+    return (__float_as_uint(x) >> 24) & 0x80u;
+}
+
+// Quantise four values of a block with dequant scale sc (sc > 0 or sc == 0).
+// Division is IEEE binary32 round-to-nearest-even (hipcc's default).
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float sc)
+{
+    if (sc == 0.0f)
+        return sign_code(a) | (sign_code(b) << 8) | (sign_code(c) << 16) | (sign_code(d) << 24);
+    return e4m3x4(a / sc, b / sc, c / sc, d / sc);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Round to nearest even FP32 -> BF16 (finite inputs), as a 16-bit pattern.
+__device__ __forceinline__ uint16_t to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Element loads widened to FP32.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float *p) { return *p; }
+    // 8 consecutive values from a 16-byte aligned address
+    __device__ __forceinline__ static void load8(const float *p, float v[8])
+    {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+    __device__ __forceinline__ static void load8(const uint16_t *p, float v[8])
+    {
+        const uint4 a = *reinterpret_cast<const uint4 *>(p);
+        v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+        v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+    }
+};
+
+} // namespace puro

@@ -1,0 +1,302 @@
+// Blockwise-scaled E4M3 GEMM on the gfx950 matrix cores.
+//
+//   C[m][n] = sum_kb sA(m,kb) * sB(n,kb) * P_kb[m][n],
+//   P_kb[m][n] = sum_{k in block kb} a(m,k) b(k,n)
+//
+// P_kb (one 128-wide K block) is formed on the matrix cores from a zero
+// accumulator, then promoted into FP32 accumulators with one FMA per element:
+// acc = fma(sA*sB, P_kb, acc).  This is the FP8 linear-layer GEMM of the
+// Puro-2B-Base model card's setup paragraph (blockwise E4M3, FP32 kept where
+// needed), with the per-block promotion of the DeepSeek-V3 design the
+// technical report's related-work paragraph cites.
+//
+// Two matrix-core datapaths form P_kb from the same E4M3 fragments:
+//  * F16 (default): each E4M3 code is widened to FP16 in registers
+//    (v_cvt_scalef32_pk_f16_fp8, exact: every E4M3 value is an FP16 value) and
+//    P_kb is four chained v_mfma_f32_16x16x32_f16.  Measured on gfx950, these
+//    sums are FP32-grade (relative error ~1e-8 on quantised data).
+//  * FP8 (native): one v_mfma_f32_16x16x128_f8f6f4.  Twice the peak rate, but
+//    measured on gfx950 it adds each run of 8 consecutive products in a
+//    fixed-point window about 13 bits below the largest of them, so small
+//    products next to large ones are truncated (relative error ~1e-5 to 1e-4
+//    on quantised data).
+//
+// Register layouts, measured on gfx950: for v_mfma_f32_16x16x128_f8f6f4 lane l
+// holds A row l%16 and B column l%16, bytes 0..31 being K slots
+// 32*(l/16) .. +31 (the same K index in A and B); result register r of lane l
+// is P[4*(l/16) + r][l%16].  The F16 path feeds bytes 8c .. 8c+7 of the same
+// fragments to MFMA c (c = 0..3), keeping A and B K-aligned, with the same
+// result layout.
+//
+// Operands whose K dimension is contiguous are staged in LDS as [row][128 k]
+// with a 16-byte XOR swizzle and read with 16-byte loads; operands whose M or
+// N dimension is contiguous (B of NN, A and B of TN) are staged as
+// [128 k][row] and read with ds_read_b64_tr_b8, whose 8x16-byte transpose
+// within each 16-lane group yields the same K-contiguous fragments.
+#include "common.h"
+#include "kernels.h"
+
+namespace puro {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 128;
+
+struct GemmArgs {
+    const uint8_t *A;
+    const uint8_t *B;
+    const float *sA;
+    const float *sB;
+    void *C;
+    int64_t M, N, K, lda, ldb, ldc, KB, NB;
+};
+
+// Stage a 128 x 128-byte tile of a row-major byte matrix into LDS.
+//   rows [row0, row0+128) limited to nrows, bytes [col0, col0+128) limited to ncols;
+//   out-of-range bytes are zero.  SWZ: 16-byte segment index XOR (row & 7).
+template <bool SWZ>
+__device__ __forceinline__ void stage_tile(uint8_t *lds, const uint8_t *g, int64_t ld,
+                                           int64_t row0, int64_t nrows, int64_t col0,
+                                           int64_t ncols, int tid)
+{
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+        const int chunk = tid + 256 * it;
+        const int row = chunk >> 3, seg = chunk & 7;
+        const int64_t gr = row0 + row, gc = col0 + seg * 16;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (gr < nrows) {
+            const uint8_t *src = g + gr * ld + gc;
+            if (gc + 16 <= ncols) {
+                val = *reinterpret_cast<const uint4 *>(src);
+            } else if (gc < ncols) {
+                uint32_t w[4] = {0, 0, 0, 0};
+                for (int e = 0; e < 16; e++)
+                    if (gc + e < ncols)
+                        w[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
+                val = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        const int pseg = SWZ ? (seg ^ (row & 7)) : seg;
+        *reinterpret_cast<uint4 *>(lds + row * 128 + pseg * 16) = val;
+    }
+}
+
+// Fragment of a K-contiguous tile ([row][128 k], swizzled): 16 rows from row_base.
+__device__ __forceinline__ v8i frag_kmajor(const uint8_t *lds, int row_base, int lane)
+{
+    const int row = row_base + (lane & 15);
+    const int g = lane >> 4;
+    const int s0 = (2 * g) ^ (row & 7), s1 = (2 * g + 1) ^ (row & 7);
+    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + row * 128 + s0 * 16);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + row * 128 + s1 * 16);
+    v8i f;
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    return f;
+}
+
+// Fragment of an MN-contiguous tile ([128 k][128 mn], unswizzled): 16 columns from col_base.
+__device__ __forceinline__ v8i frag_mnmajor(const uint8_t *lds, int col_base, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    v8i f;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const int k = 32 * g + 8 * t + (i >> 1);
+        const int c = col_base + 8 * (i & 1);
+        typedef __attribute__((address_space(3))) v2i lds_v2i;
+        const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(lds + k * 128 + c));
+        f[2 * t] = r[0];
+        f[2 * t + 1] = r[1];
+    }
+    return f;
+}
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Bytes 8c .. 8c+7 of an E4M3 fragment as eight FP16 values (exact).
+__device__ __forceinline__ v8h widen8(const v8i &f, int c)
+{
+    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)f[2 * c], 1.0f, false);
+    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)f[2 * c], 1.0f, true);
+    const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)f[2 * c + 1], 1.0f, false);
+    const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)f[2 * c + 1], 1.0f, true);
+    v8h r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = d[0]; r[5] = d[1]; r[6] = e[0]; r[7] = e[1];
+    return r;
+}
+
+// Sum over one 128-wide K block of a(m,k) b(k,n) for a 16x16 output tile.
+template <bool NATIVE_FP8>
+__device__ __forceinline__ v4f block_partial(const v8i &a, const v8i &b)
+{
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (NATIVE_FP8)
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+    v4f p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 0), widen8(b, 0), zero, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 1), widen8(b, 1), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 2), widen8(b, 2), p, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 3), widen8(b, 3), p, 0, 0, 0);
+}
+
+template <int LAYOUT, int BGRAN, bool CBF16, bool NATIVE_FP8>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
+{
+    constexpr bool A_KMAJ = (LAYOUT != 2);
+    constexpr bool B_KMAJ = (LAYOUT == 0);
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * BK];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[BN * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+
+    float acc[4][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                acc[i][j][r] = 0.0f;
+
+    // Rows (m) and columns (n) of this lane's accumulator elements.
+    int64_t mrow[4][4], ncol[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            mrow[i][r] = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        ncol[j] = n0 + wn * 64 + j * 16 + (lane & 15);
+
+    for (int64_t kb = 0; kb < p.KB; kb++) {
+        const int64_t k0 = kb * BK;
+        __syncthreads();
+        if (A_KMAJ)
+            stage_tile<true>(lds_a, p.A, p.lda, m0, p.M, k0, p.K, tid);
+        else
+            stage_tile<false>(lds_a, p.A, p.lda, k0, p.K, m0, p.M, tid);
+        if (B_KMAJ)
+            stage_tile<true>(lds_b, p.B, p.ldb, n0, p.N, k0, p.K, tid);
+        else
+            stage_tile<false>(lds_b, p.B, p.ldb, k0, p.K, n0, p.N, tid);
+        __syncthreads();
+
+        // Scales of this K block for this lane's rows and columns.
+        float sa[4][4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int64_t m = mrow[i][r];
+                sa[i][r] = (m < p.M) ? (A_KMAJ ? p.sA[m * p.KB + kb] : p.sA[kb * p.M + m]) : 0.0f;
+            }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t n = ncol[j];
+            float v = 0.0f;
+            if (n < p.N) {
+                if (LAYOUT == 0)
+                    v = BGRAN ? p.sB[(n >> 7) * p.KB + kb] : p.sB[n * p.KB + kb];
+                else
+                    v = BGRAN ? p.sB[kb * p.NB + (n >> 7)] : p.sB[kb * p.N + n];
+            }
+            sb[j] = v;
+        }
+
+        v8i af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            af[i] = A_KMAJ ? frag_kmajor(lds_a, wm * 64 + i * 16, lane)
+                           : frag_mnmajor(lds_a, wm * 64 + i * 16, lane);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            bf[j] = B_KMAJ ? frag_kmajor(lds_b, wn * 64 + j * 16, lane)
+                           : frag_mnmajor(lds_b, wn * 64 + j * 16, lane);
+
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const v4f P = block_partial<NATIVE_FP8>(af[i], bf[j]);
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    acc[i][j][r] = fmaf(sa[i][r] * sb[j], P[r], acc[i][j][r]);
+            }
+    }
+
+    // Epilogue: FP32 or BF16 (round to nearest even).
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t m = mrow[i][r];
+            if (m >= p.M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int64_t n = ncol[j];
+                if (n >= p.N)
+                    continue;
+                if (CBF16)
+                    reinterpret_cast<uint16_t *>(p.C)[m * p.ldc + n] = to_bf16(acc[i][j][r]);
+                else
+                    reinterpret_cast<float *>(p.C)[m * p.ldc + n] = acc[i][j][r];
+            }
+        }
+}
+
+template <int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_one(const GemmArgs &a, hipStream_t st)
+{
+    const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+    hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int LAYOUT>
+hipError_t launch_layout(const GemmProblem &p, const GemmArgs &a, hipStream_t st)
+{
+    if (p.bgran)
+        return p.c_bf16 ? launch_one<LAYOUT, 1, true>(a, st) : launch_one<LAYOUT, 1, false>(a, st);
+    return p.c_bf16 ? launch_one<LAYOUT, 0, true>(a, st) : launch_one<LAYOUT, 0, false>(a, st);
+}
+
+} // namespace
+
+size_t gemm_workspace_bytes(const GemmProblem &)
+{
+    return 0;
+}
+
+hipError_t launch_gemm(const GemmProblem &p, void *, hipStream_t st)
+{
+    if (p.M == 0 || p.N == 0)
+        return hipSuccess;
+    GemmArgs a;
+    a.A = p.A;
+    a.B = p.B;
+    a.sA = p.sA;
+    a.sB = p.sB;
+    a.C = p.C;
+    a.M = p.M;
+    a.N = p.N;
+    a.K = p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.KB = (p.K + 127) / 128;
+    a.NB = (p.N + 127) / 128;
+    switch (p.layout) {
+    case 0: return launch_layout<0>(p, a, st);
+    case 1: return launch_layout<1>(p, a, st);
+    default: return launch_layout<2>(p, a, st);
+    }
+}
+
+} // namespace puro

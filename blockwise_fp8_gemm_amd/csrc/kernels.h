@@ -1,0 +1,37 @@
+// Internal launchers (host side).  Arguments are validated by the C-ABI layer
+// before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace puro {
+
+hipError_t launch_quant_act(const void *x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
+                            uint8_t *q, int64_t ldq, float *s, hipStream_t st);
+hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t cols, int64_t ldw,
+                               uint8_t *q, int64_t ldq, float *s, hipStream_t st);
+hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int64_t cols,
+                                  int64_t ldx, bool transpose_out, uint8_t *q, int64_t ldq,
+                                  float *s, hipStream_t st);
+
+struct GemmProblem {
+    int layout;   // 0 NT, 1 NN, 2 TN
+    int bgran;    // 0 1x128, 1 128x128
+    bool c_bf16;  // output dtype
+    int64_t M, N, K;
+    const uint8_t *A;
+    int64_t lda;
+    const float *sA;
+    const uint8_t *B;
+    int64_t ldb;
+    const float *sB;
+    void *C;
+    int64_t ldc;
+};
+
+size_t gemm_workspace_bytes(const GemmProblem &p);
+hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st);
+
+} // namespace puro

@@ -1,0 +1,137 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every call
+include/puro_fp8.h declares, and rejects bad arguments before any launch.
+
+Every call made here either fails validation or has nothing to do (empty
+extents), so no HIP work is ever enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import blockwise_fp8_gemm_amd as pf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "puro_fp8.h")
+
+OK, NULL, SHAPE, ALIGN, ENUM, WORKSPACE = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p(1 << 20)   # 16-byte aligned, never dereferenced (validation fails first)
+P_ODD = ctypes.c_void_p((1 << 20) + 4)
+NUL = ctypes.c_void_p(0)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n;]*?\b(puro_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ("puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_quant_transpose",
+              "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_status_string",
+              "puro_fp8_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = pf.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pf.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(_declared()) <= exported
+
+
+def test_status_strings():
+    for st in range(8):
+        assert pf.puro_status_string(st)
+    assert pf.puro_status_string(99) == "unknown status"
+    assert pf.puro_fp8_version() == 100
+
+
+def _qa(x=P, dt=1, rows=4, cols=128, ldx=128, q=P, ldq=128, s=P):
+    return pf.lib().puro_fp8_quant_act(x, dt, rows, cols, ldx, q, ldq, s, None)
+
+
+def _qw(x=P, dt=0, rows=128, cols=128, ldx=128, q=P, ldq=128, s=P):
+    return pf.lib().puro_fp8_quant_weight(x, dt, rows, cols, ldx, q, ldq, s, None)
+
+
+def _qt(x=P, dt=1, tokens=256, cols=64, ldx=64, t=1, q=P, ldq=256, s=P):
+    return pf.lib().puro_fp8_quant_transpose(x, dt, tokens, cols, ldx, t, q, ldq, s, None)
+
+
+@pytest.mark.parametrize("fn", [_qa, _qw])
+def test_quant_validation(fn):
+    assert fn(dt=2) == ENUM
+    assert fn(dt=-1) == ENUM
+    assert fn(rows=-1) == SHAPE
+    assert fn(cols=-5) == SHAPE
+    assert fn(ldx=64) == SHAPE
+    assert fn(ldq=64) == SHAPE
+    assert fn(rows=1 << 24) == SHAPE
+    assert fn(x=NUL) == NULL
+    assert fn(q=NUL) == NULL
+    assert fn(s=NUL) == NULL
+    assert fn(ldx=136) == ALIGN
+    assert fn(ldq=136) == ALIGN
+    assert fn(x=P_ODD) == ALIGN
+    assert fn(q=P_ODD) == ALIGN
+    assert fn(s=ctypes.c_void_p((1 << 20) + 2)) == ALIGN
+    # empty: nothing to do, NULL pointers allowed
+    assert fn(x=NUL, q=NUL, s=NUL, rows=0) == OK
+    assert fn(x=NUL, q=NUL, s=NUL, cols=0, ldx=0, ldq=0) == OK
+
+
+def test_quant_transpose_validation():
+    assert _qt(t=2) == ENUM
+    assert _qt(t=-1) == ENUM
+    assert _qt(dt=5) == ENUM
+    assert _qt(ldq=128) == SHAPE          # transposed output rows hold `tokens` codes
+    assert _qt(t=0, ldq=32) == SHAPE      # untransposed output rows hold `cols` codes
+    assert _qt(ldx=32) == SHAPE
+    assert _qt(x=NUL) == NULL
+    assert _qt(ldq=264) == ALIGN
+    assert _qt(x=NUL, q=NUL, s=NUL, tokens=0, ldq=0) == OK
+
+
+def _gemm(layout=0, M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, bg=1, C=P,
+          cdt=1, ldc=256, ws=NUL, wsb=0):
+    return pf.lib().puro_fp8_gemm(layout, M, N, K, A, lda, sA, B, ldb, sB, bg, C, cdt, ldc, ws,
+                                  wsb, None)
+
+
+def test_gemm_validation():
+    assert _gemm(layout=3) == ENUM
+    assert _gemm(bg=2) == ENUM
+    assert _gemm(cdt=7) == ENUM
+    assert _gemm(M=-1) == SHAPE
+    assert _gemm(K=1 << 24) == SHAPE
+    assert _gemm(lda=128) == SHAPE
+    assert _gemm(ldb=128) == SHAPE
+    assert _gemm(ldc=128) == SHAPE
+    assert _gemm(layout=2, M=512, lda=256) == SHAPE       # TN: A rows hold M codes
+    assert _gemm(layout=1, N=512, ldb=256) == SHAPE       # NN: B rows hold N codes
+    assert _gemm(A=NUL) == NULL
+    assert _gemm(sA=NUL) == NULL
+    assert _gemm(B=NUL) == NULL
+    assert _gemm(sB=NUL) == NULL
+    assert _gemm(C=NUL) == NULL
+    assert _gemm(lda=264) == ALIGN
+    assert _gemm(ldc=264) == ALIGN
+    assert _gemm(A=P_ODD) == ALIGN
+    assert _gemm(C=P_ODD) == ALIGN
+    assert _gemm(sB=ctypes.c_void_p((1 << 20) + 1)) == ALIGN
+    # empty products: nothing enqueued
+    assert _gemm(M=0, A=NUL, sA=NUL, C=NUL) == OK
+    assert _gemm(N=0, B=NUL, sB=NUL, C=NUL, ldb=256, ldc=0) == OK
+
+
+def test_workspace_size_is_defined_for_every_layout():
+    for layout in ("NT", "NN", "TN"):
+        for bg in ("1x128", "128x128"):
+            assert pf.puro_fp8_gemm_workspace_size(layout, 8192, 2048, 8192, bg) >= 0
+    assert pf.lib().puro_fp8_gemm_workspace_size(9, 128, 128, 128, 0) == 0
