@@ -251,9 +251,245 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
         }
 }
 
+// ===========================================================================
+// Fast path for aligned problems (M % 256 == 0, N % 128 == 0, K % 128 == 0).
+//
+// Workgroup tile 256 x 128, four waves in a 2 x 2 arrangement, 128 x 64 per
+// wave (8 x 4 MFMA tiles of 16 x 16).  Each 128-wide K block of A and B is
+// copied straight from HBM into LDS with global_load_lds_dwordx4 (lane l's 16
+// bytes land at the wave's LDS base + 16 l, so lanes fetch permuted global
+// addresses to produce the swizzled layout), double-buffered so that block
+// kb+1 streams in while block kb is multiplied; one barrier per K block.
+// The block's scales travel the same way (4-byte direct loads).
+//
+// LDS layouts (bank-conflict-free fragment reads):
+//   K-major tile [rows][128 B]: segment s of row r at s ^ ((r >> 1) & 7)
+//   MN-major tile [128 k][W B]: segment s of row k at s ^ (k & 7)
+// ===========================================================================
+
+constexpr int FM = 256, FN = 128;
+constexpr int FA_BYTES = FM * 128, FB_BYTES = FN * 128;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v2i lds_v2i_t;
+
+__device__ __forceinline__ void load_lds16(const void *g, uint8_t *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void load_lds4(const void *g, void *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_wave_base, 4, 0, 0);
+}
+
+// Rows [row0, row0+ROWS) x bytes [k0, k0+128) of a K-contiguous operand.
+template <int ROWS>
+__device__ __forceinline__ void fast_stage_k(uint8_t *t, const uint8_t *g, int64_t ld, int64_t row0,
+                                             int64_t k0, int wave, int lane)
+{
+#pragma unroll
+    for (int c = wave; c < ROWS / 8; c += 4) {
+        const int row = c * 8 + (lane >> 3);
+        const int seg = (lane & 7) ^ ((row >> 1) & 7);
+        load_lds16(g + (row0 + row) * ld + k0 + seg * 16, t + c * 1024);
+    }
+}
+
+// Rows k [k0, k0+128) x bytes [mn0, mn0+W) of an M- or N-contiguous operand.
+template <int W>
+__device__ __forceinline__ void fast_stage_mn(uint8_t *t, const uint8_t *g, int64_t ld, int64_t k0,
+                                              int64_t mn0, int wave, int lane)
+{
+    constexpr int SEGS = W / 16, RPC = 1024 / W;
+#pragma unroll
+    for (int c = wave; c < 128 / RPC; c += 4) {
+        const int row = c * RPC + lane / SEGS;
+        const int seg = (lane % SEGS) ^ (row & 7);
+        load_lds16(g + (k0 + row) * ld + mn0 + seg * 16, t + c * 1024);
+    }
+}
+
+__device__ __forceinline__ v8i fast_frag_k(const uint8_t *t, int row_base, int lane)
+{
+    const int row = row_base + (lane & 15);
+    const int g = lane >> 4, f = (row >> 1) & 7;
+    const uint4 lo = *reinterpret_cast<const uint4 *>(t + row * 128 + (((2 * g) ^ f) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(t + row * 128 + (((2 * g + 1) ^ f) << 4));
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+template <int W>
+__device__ __forceinline__ v8i fast_frag_mn(const uint8_t *t, int col_base, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    const int seg = (col_base >> 4), within = 8 * (i & 1);
+    v8i r;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int k = 32 * g + 8 * q + (i >> 1);
+        const uint8_t *a = t + k * W + ((seg ^ (k & 7)) << 4) + within;
+        const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)a);
+        r[2 * q] = v[0];
+        r[2 * q + 1] = v[1];
+    }
+    return r;
+}
+
+struct V8H4 {
+    v8h c[4];
+};
+
+__device__ __forceinline__ V8H4 widen32(const v8i &f)
+{
+    V8H4 h;
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+        h.c[q] = widen8(f, q);
+    return h;
+}
+
+template <int LAYOUT, int BGRAN, bool CBF16>
+__global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n)
+{
+    constexpr bool A_KMAJ = (LAYOUT != 2);
+    constexpr bool B_KMAJ = (LAYOUT == 0);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][FA_BYTES + FB_BYTES];
+    __shared__ __attribute__((aligned(16))) float lds_sa[2][FM];
+    __shared__ __attribute__((aligned(16))) float lds_sb[2][FN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Tile order: workgroups are dispatched round-robin over the 8 XCDs; give
+    // each XCD a contiguous run of tiles, walked in groups of 8 tile rows so
+    // that workgroups resident together share A and B panels in that XCD's L2.
+    const int nwg = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if ((nwg & 7) == 0)
+        t = (t & 7) * (nwg >> 3) + (t >> 3);
+    constexpr int GROUP = 8;
+    const int group = t / (GROUP * tiles_n);
+    const int first_m = group * GROUP;
+    const int gm = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (t % (GROUP * tiles_n)) % gm;
+    const int tn = (t % (GROUP * tiles_n)) / gm;
+    const int64_t m0 = (int64_t)tm * FM, n0 = (int64_t)tn * FN;
+
+    float acc[8][4][4];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                acc[i][j][r] = 0.0f;
+
+    auto stage = [&](int64_t kb, int buf) {
+        const int64_t k0 = kb * 128;
+        uint8_t *ta = lds[buf];
+        uint8_t *tb = lds[buf] + FA_BYTES;
+        if (A_KMAJ)
+            fast_stage_k<FM>(ta, p.A, p.lda, m0, k0, wave, lane);
+        else
+            fast_stage_mn<FM>(ta, p.A, p.lda, k0, m0, wave, lane);
+        if (B_KMAJ)
+            fast_stage_k<FN>(tb, p.B, p.ldb, n0, k0, wave, lane);
+        else
+            fast_stage_mn<FN>(tb, p.B, p.ldb, k0, n0, wave, lane);
+        // scales of A: 256 rows, one 4-byte direct load per lane
+        const int64_t m = m0 + tid;
+        load_lds4(A_KMAJ ? (const void *)(p.sA + m * p.KB + kb) : (const void *)(p.sA + kb * p.M + m),
+                  &lds_sa[buf][wave * 64]);
+        if (!BGRAN && wave < 2) {
+            const int64_t n = n0 + tid;
+            load_lds4(B_KMAJ ? (const void *)(p.sB + n * p.KB + kb) : (const void *)(p.sB + kb * p.N + n),
+                      &lds_sb[buf][wave * 64]);
+        }
+    };
+
+    stage(0, 0);
+    for (int64_t kb = 0; kb < p.KB; kb++) {
+        const int buf = (int)(kb & 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of block kb have landed
+        __syncthreads();                 // ... and everyone's; block kb-1 is no longer read
+        if (kb + 1 < p.KB)
+            stage(kb + 1, buf ^ 1);
+
+        const uint8_t *ta = lds[buf];
+        const uint8_t *tb = lds[buf] + FA_BYTES;
+
+        float sbv[4];
+        if (BGRAN) {
+            const float v = B_KMAJ ? p.sB[(n0 >> 7) * p.KB + kb] : p.sB[kb * p.NB + (n0 >> 7)];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                sbv[j] = v;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                sbv[j] = lds_sb[buf][wn * 64 + j * 16 + (lane & 15)];
+        }
+
+        V8H4 bh[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            bh[j] = widen32(B_KMAJ ? fast_frag_k(tb, wn * 64 + j * 16, lane)
+                                   : fast_frag_mn<FN>(tb, wn * 64 + j * 16, lane));
+
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const V8H4 ah = widen32(A_KMAJ ? fast_frag_k(ta, wm * 128 + i * 16, lane)
+                                           : fast_frag_mn<FM>(ta, wm * 128 + i * 16, lane));
+            const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sa[buf][wm * 128 + i * 16 + 4 * (lane >> 4)]);
+            const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                v4f P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[0], bh[j].c[0], zero, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[1], bh[j].c[1], P, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[2], bh[j].c[2], P, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[3], bh[j].c[3], P, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    acc[i][j][r] = fmaf(sa[r] * sbv[j], P[r], acc[i][j][r]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t m = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + r;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+                if (CBF16)
+                    reinterpret_cast<uint16_t *>(p.C)[m * p.ldc + n] = to_bf16(acc[i][j][r]);
+                else
+                    reinterpret_cast<float *>(p.C)[m * p.ldc + n] = acc[i][j][r];
+            }
+        }
+}
+
+template <int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_fast(const GemmArgs &a, hipStream_t st)
+{
+    const int tiles_m = (int)(a.M / FM), tiles_n = (int)(a.N / FN);
+    hipLaunchKernelGGL((gemm_fast_kernel<LAYOUT, BGRAN, CBF16>), dim3(tiles_m * tiles_n), dim3(256), 0,
+                       st, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_one(const GemmArgs &a, hipStream_t st)
 {
+    if (a.M % FM == 0 && a.N % FN == 0 && a.K % 128 == 0 && a.K > 0)
+        return launch_fast<LAYOUT, BGRAN, CBF16>(a, st);
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
     hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
     return hipGetLastError();

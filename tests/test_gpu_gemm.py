@@ -7,7 +7,7 @@ quantisers (bit-identical, checked first).  Tolerances:
     per element |C - C_ref| <= E = (KB + 4) 2^-23 C_abs, the FP32 accumulation
     bound for KB block promotions, where C_abs is the same blockwise product
     of |a|, |b| (so E bounds rounding in the sum of absolute terms);
-  * BF16 output: per element |C - C_ref| <= E + 2^-9 (|C_ref| + E) (the FP32
+  * BF16 output: per element |C - C_ref| <= E + 2^-8 (|C_ref| + E) (the FP32
     bound plus one BF16 rounding), and at least 99% of elements equal to the
     oracle's FP64 result rounded to BF16.
 """
@@ -84,7 +84,7 @@ def _check_product(layout, bgran, hostops, devops, out):
     else:
         bits = host(C)
         got = bf16_to_f64(bits)
-        bad = np.argwhere(np.abs(got - C_ref) > E + 2.0 ** -9 * (np.abs(C_ref) + E))
+        bad = np.argwhere(np.abs(got - C_ref) > E + 2.0 ** -8 * (np.abs(C_ref) + E))
         assert bad.size == 0, ("element bound", tuple(bad[0]))
         exact = (bits == oracle.bf16_rne(C_ref)).mean()
         assert exact >= 0.99, exact
@@ -93,6 +93,7 @@ def _check_product(layout, bgran, hostops, devops, out):
 
 SHAPES = [
     ("config1", 256, 256, 512),
+    ("aligned_2x3", 512, 384, 768),
     ("tiles_3x2", 384, 256, 640),
     ("ragged", 200, 136, 300),
     ("ragged_thin", 130, 7, 1000),
