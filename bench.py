@@ -83,6 +83,16 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     dw = {g: torch.empty((n, k), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, y, dx, dw]
 
+    # one workspace for every call that splits K (calls run in stream order)
+    ws_bytes = 0
+    for g, n, k, _ in synth.LAYER_GEMMS:
+        ws_bytes = max(ws_bytes, pf.puro_fp8_gemm_workspace_size("NT", tokens, n, k, "128x128"),
+                       pf.puro_fp8_gemm_workspace_size("NN", tokens, k, n, "128x128"),
+                       pf.puro_fp8_gemm_workspace_size("NT", n, k, tokens, "1x128"))
+    ws = torch.empty(max(ws_bytes, 256), dtype=u8, device=dev)
+    keep.append(ws)
+    WS, WSB = P(ws), ctypes.c_size_t(ws_bytes)
+
     BF16, F32 = pf.PURO_BF16, pf.PURO_F32
     NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
     S1, S128 = pf.BGRAN["1x128"], pf.BGRAN["128x128"]
@@ -90,27 +100,27 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     for layer in range(layers):
         xs = {name: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
               for i, (name, c) in enumerate(synth.LAYER_INPUTS)}
-        ws = {g: synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
-              for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
+        wts = {g: synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
+               for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
         dys = {g: synth.device_normal((T, n), 1e-3, synth.seed_of(4, layer, 20 + j), "bf16", dev)
                for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
-        keep += [xs, ws, dys]
+        keep += [xs, wts, dys]
         # forward: quantise each distinct input once, each weight once, then Y = X W^T
         for name, c in synth.LAYER_INPUTS:
             plan.add(L.puro_fp8_quant_act, (P(xs[name]), BF16, T, c, c, P(qx[name]), c, P(sx[name]),
                                             stream_ptr), "quant_act", "quant_act", 0, T * c * (2 + 1 + 4 / 128))
         for g, n, k, src in synth.LAYER_GEMMS:
-            plan.add(L.puro_fp8_quant_weight, (P(ws[g]), F32, n, k, k, P(qw[g]), k, P(sw[g]), stream_ptr),
+            plan.add(L.puro_fp8_quant_weight, (P(wts[g]), F32, n, k, k, P(qw[g]), k, P(sw[g]), stream_ptr),
                      "quant_weight", "quant_weight", 0, n * k * (4 + 1) + nb(n) * nb(k) * 4)
             plan.add(L.puro_fp8_gemm, (NT, T, n, k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]),
-                                       S128, P(y[g]), BF16, n, None, 0, stream_ptr),
+                                       S128, P(y[g]), BF16, n, WS, WSB, stream_ptr),
                      "gemm", "gemm_fwd_NT_128x128_bf16", 2.0 * T * n * k)
         # data gradient: dX = dY W with the forward's quantised W
         for g, n, k, src in synth.LAYER_GEMMS:
             plan.add(L.puro_fp8_quant_act, (P(dys[g]), BF16, T, n, n, P(qdy), n, P(sdy), stream_ptr),
                      "quant_act", "quant_act", 0, T * n * (2 + 1 + 4 / 128))
             plan.add(L.puro_fp8_gemm, (NN, T, k, n, P(qdy), n, P(sdy), P(qw[g]), k, P(sw[g]), S128,
-                                       P(dx[g]), BF16, k, None, 0, stream_ptr),
+                                       P(dx[g]), BF16, k, WS, WSB, stream_ptr),
                      "gemm", "gemm_dgrad_NN_128x128_bf16", 2.0 * T * n * k)
         # weight gradient: dW = dY^T X on token-blocked copies
         for name, c in synth.LAYER_INPUTS:
@@ -122,7 +132,7 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
                                                   stream_ptr),
                      "quant_transpose", "quant_transpose", 0, T * n * (2 + 1 + 4 / 128))
             plan.add(L.puro_fp8_gemm, (NT, n, k, T, P(qdyt), T, P(sdyt), P(qxt[src]), T, P(sxt[src]),
-                                       S1, P(dw[g]), F32, k, None, 0, stream_ptr),
+                                       S1, P(dw[g]), F32, k, WS, WSB, stream_ptr),
                      "gemm", "gemm_wgrad_NT_1x128_f32", 2.0 * T * n * k)
     return plan, keep
 

@@ -252,23 +252,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
 }
 
 // ===========================================================================
-// Fast path for aligned problems (M % 256 == 0, N % 128 == 0, K % 128 == 0).
+// Fast path for aligned problems (M % TM == 0, N % TN == 0, K % 128 == 0).
 //
-// Workgroup tile 256 x 128, four waves in a 2 x 2 arrangement, 128 x 64 per
-// wave (8 x 4 MFMA tiles of 16 x 16).  Each 128-wide K block of A and B is
-// copied straight from HBM into LDS with global_load_lds_dwordx4 (lane l's 16
-// bytes land at the wave's LDS base + 16 l, so lanes fetch permuted global
-// addresses to produce the swizzled layout), double-buffered so that block
-// kb+1 streams in while block kb is multiplied; one barrier per K block.
-// The block's scales travel the same way (4-byte direct loads).
+// Workgroup tile TM x TN computed by WM x WN waves, each wave IT x JT MFMA
+// tiles of 16 x 16 (so (16 IT) x (16 JT) outputs).  Each 128-wide K block of
+// A and B is copied straight from HBM into LDS with global_load_lds_dwordx4
+// (lane l's 16 bytes land at the wave's LDS base + 16 l, so lanes fetch
+// permuted global addresses to produce the swizzled layout), double-buffered
+// so that block kb+1 streams in while block kb is multiplied; one barrier per
+// K block.  The block's scales travel the same way (4-byte direct loads).
 //
 // LDS layouts (bank-conflict-free fragment reads):
 //   K-major tile [rows][128 B]: segment s of row r at s ^ ((r >> 1) & 7)
 //   MN-major tile [128 k][W B]: segment s of row k at s ^ (k & 7)
 // ===========================================================================
-
-constexpr int FM = 256, FN = 128;
-constexpr int FA_BYTES = FM * 128, FB_BYTES = FN * 128;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v2i lds_v2i_t;
@@ -283,27 +280,31 @@ __device__ __forceinline__ void load_lds4(const void *g, void *lds_wave_base)
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_wave_base, 4, 0, 0);
 }
 
-// Rows [row0, row0+ROWS) x bytes [k0, k0+128) of a K-contiguous operand.
-template <int ROWS>
+// Rows [row0, row0+ROWS) x bytes [k0, k0+128) of a K-contiguous operand, NW waves.
+template <int ROWS, int NW>
 __device__ __forceinline__ void fast_stage_k(uint8_t *t, const uint8_t *g, int64_t ld, int64_t row0,
                                              int64_t k0, int wave, int lane)
 {
+    static_assert((ROWS / 8) % NW == 0, "whole 1 KB chunks per wave");
 #pragma unroll
-    for (int c = wave; c < ROWS / 8; c += 4) {
+    for (int it = 0; it < ROWS / 8 / NW; it++) {
+        const int c = wave + NW * it;
         const int row = c * 8 + (lane >> 3);
         const int seg = (lane & 7) ^ ((row >> 1) & 7);
         load_lds16(g + (row0 + row) * ld + k0 + seg * 16, t + c * 1024);
     }
 }
 
-// Rows k [k0, k0+128) x bytes [mn0, mn0+W) of an M- or N-contiguous operand.
-template <int W>
+// Rows k [k0, k0+128) x bytes [mn0, mn0+W) of an M- or N-contiguous operand, NW waves.
+template <int W, int NW>
 __device__ __forceinline__ void fast_stage_mn(uint8_t *t, const uint8_t *g, int64_t ld, int64_t k0,
                                               int64_t mn0, int wave, int lane)
 {
     constexpr int SEGS = W / 16, RPC = 1024 / W;
+    static_assert((128 / RPC) % NW == 0, "whole 1 KB chunks per wave");
 #pragma unroll
-    for (int c = wave; c < 128 / RPC; c += 4) {
+    for (int it = 0; it < 128 / RPC / NW; it++) {
+        const int c = wave + NW * it;
         const int row = c * RPC + lane / SEGS;
         const int seg = (lane % SEGS) ^ (row & 7);
         load_lds16(g + (k0 + row) * ld + mn0 + seg * 16, t + c * 1024);
@@ -352,38 +353,62 @@ __device__ __forceinline__ V8H4 widen32(const v8i &f)
     return h;
 }
 
-template <int LAYOUT, int BGRAN, bool CBF16>
-__global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n)
+template <int WM_, int WN_, int IT_, int JT_>
+struct FastCfg {
+    static constexpr int WM = WM_, WN = WN_, IT = IT_, JT = JT_;
+    static constexpr int NW = WM * WN, THREADS = 64 * NW;
+    static constexpr int TM = WM * IT * 16, TN = WN * JT * 16;
+    static constexpr int A_BYTES = TM * 128, B_BYTES = TN * 128;
+};
+
+// 256 x 256 workgroup tiles (8 waves of 128 x 64) for large outputs, 256 x 128
+// (8 waves of 64 x 64) where 256 x 256 would leave compute units idle.
+typedef FastCfg<2, 4, 8, 4> CfgL;
+typedef FastCfg<4, 2, 4, 4> CfgS;
+
+// Split-K: workgroup b handles K blocks [kb_lo, kb_hi) of split s = b / tiles
+// and, with OUT_PARTIAL, stores FP32 partial sums to ws[s][M][N] (row stride N)
+// instead of C; gemm_split_reduce then adds the splits in order.
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL>
+__global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n,
+                                                                 int splits, float *ws)
 {
     constexpr bool A_KMAJ = (LAYOUT != 2);
     constexpr bool B_KMAJ = (LAYOUT == 0);
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][FA_BYTES + FB_BYTES];
-    __shared__ __attribute__((aligned(16))) float lds_sa[2][FM];
-    __shared__ __attribute__((aligned(16))) float lds_sb[2][FN];
+    constexpr int NW = Cfg::NW, TM = Cfg::TM, TN = Cfg::TN, IT = Cfg::IT, JT = Cfg::JT;
+    constexpr int A_BYTES = Cfg::A_BYTES, B_BYTES = Cfg::B_BYTES;
+    static_assert(TN % 128 == 0 || !BGRAN || TN <= 128, "tile columns within 128-wide weight tiles");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][A_BYTES + B_BYTES];
+    __shared__ __attribute__((aligned(16))) float lds_sa[2][TM];
+    __shared__ __attribute__((aligned(16))) float lds_sb[2][TN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
     // Tile order: workgroups are dispatched round-robin over the 8 XCDs; give
     // each XCD a contiguous run of tiles, walked in groups of 8 tile rows so
     // that workgroups resident together share A and B panels in that XCD's L2.
-    const int nwg = tiles_m * tiles_n;
-    int t = blockIdx.x;
+    const int tiles = tiles_m * tiles_n;
+    const int nwg = tiles * splits;
+    int b = blockIdx.x;
     if ((nwg & 7) == 0)
-        t = (t & 7) * (nwg >> 3) + (t >> 3);
+        b = (b & 7) * (nwg >> 3) + (b >> 3);
+    const int split = b / tiles;
+    int t = b - split * tiles;
+    const int64_t kb_lo = p.KB * split / splits, kb_hi = p.KB * (split + 1) / splits;
     constexpr int GROUP = 8;
     const int group = t / (GROUP * tiles_n);
     const int first_m = group * GROUP;
     const int gm = min(tiles_m - first_m, GROUP);
     const int tm = first_m + (t % (GROUP * tiles_n)) % gm;
     const int tn = (t % (GROUP * tiles_n)) / gm;
-    const int64_t m0 = (int64_t)tm * FM, n0 = (int64_t)tn * FN;
+    const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
 
-    float acc[8][4][4];
+    float acc[IT][JT][4];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < IT; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < JT; j++)
 #pragma unroll
             for (int r = 0; r < 4; r++)
                 acc[i][j][r] = 0.0f;
@@ -391,63 +416,66 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs p, int tiles
     auto stage = [&](int64_t kb, int buf) {
         const int64_t k0 = kb * 128;
         uint8_t *ta = lds[buf];
-        uint8_t *tb = lds[buf] + FA_BYTES;
+        uint8_t *tb = lds[buf] + A_BYTES;
         if (A_KMAJ)
-            fast_stage_k<FM>(ta, p.A, p.lda, m0, k0, wave, lane);
+            fast_stage_k<TM, NW>(ta, p.A, p.lda, m0, k0, wave, lane);
         else
-            fast_stage_mn<FM>(ta, p.A, p.lda, k0, m0, wave, lane);
+            fast_stage_mn<TM, NW>(ta, p.A, p.lda, k0, m0, wave, lane);
         if (B_KMAJ)
-            fast_stage_k<FN>(tb, p.B, p.ldb, n0, k0, wave, lane);
+            fast_stage_k<TN, NW>(tb, p.B, p.ldb, n0, k0, wave, lane);
         else
-            fast_stage_mn<FN>(tb, p.B, p.ldb, k0, n0, wave, lane);
-        // scales of A: 256 rows, one 4-byte direct load per lane
-        const int64_t m = m0 + tid;
-        load_lds4(A_KMAJ ? (const void *)(p.sA + m * p.KB + kb) : (const void *)(p.sA + kb * p.M + m),
-                  &lds_sa[buf][wave * 64]);
-        if (!BGRAN && wave < 2) {
+            fast_stage_mn<TN, NW>(tb, p.B, p.ldb, k0, n0, wave, lane);
+        if (tid < TM) {   // scales of A: one 4-byte direct load per row
+            const int64_t m = m0 + tid;
+            load_lds4(A_KMAJ ? (const void *)(p.sA + m * p.KB + kb) : (const void *)(p.sA + kb * p.M + m),
+                      &lds_sa[buf][wave * 64]);
+        }
+        if (!BGRAN && tid < TN) {
             const int64_t n = n0 + tid;
             load_lds4(B_KMAJ ? (const void *)(p.sB + n * p.KB + kb) : (const void *)(p.sB + kb * p.N + n),
                       &lds_sb[buf][wave * 64]);
         }
     };
 
-    stage(0, 0);
-    for (int64_t kb = 0; kb < p.KB; kb++) {
-        const int buf = (int)(kb & 1);
+    stage(kb_lo, 0);
+    for (int64_t kb = kb_lo; kb < kb_hi; kb++) {
+        const int buf = (int)((kb - kb_lo) & 1);
         __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of block kb have landed
         __syncthreads();                 // ... and everyone's; block kb-1 is no longer read
-        if (kb + 1 < p.KB)
+        if (kb + 1 < kb_hi)
             stage(kb + 1, buf ^ 1);
 
         const uint8_t *ta = lds[buf];
-        const uint8_t *tb = lds[buf] + FA_BYTES;
+        const uint8_t *tb = lds[buf] + A_BYTES;
+        const int wrow = wm * IT * 16, wcol = wn * JT * 16;
 
-        float sbv[4];
+        float sbv[JT];
         if (BGRAN) {
-            const float v = B_KMAJ ? p.sB[(n0 >> 7) * p.KB + kb] : p.sB[kb * p.NB + (n0 >> 7)];
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                sbv[j] = v;
+            for (int j = 0; j < JT; j++) {
+                const int64_t nb = (n0 + wcol + j * 16) >> 7;
+                sbv[j] = B_KMAJ ? p.sB[nb * p.KB + kb] : p.sB[kb * p.NB + nb];
+            }
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                sbv[j] = lds_sb[buf][wn * 64 + j * 16 + (lane & 15)];
+            for (int j = 0; j < JT; j++)
+                sbv[j] = lds_sb[buf][wcol + j * 16 + (lane & 15)];
         }
 
-        V8H4 bh[4];
+        V8H4 bh[JT];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            bh[j] = widen32(B_KMAJ ? fast_frag_k(tb, wn * 64 + j * 16, lane)
-                                   : fast_frag_mn<FN>(tb, wn * 64 + j * 16, lane));
+        for (int j = 0; j < JT; j++)
+            bh[j] = widen32(B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane)
+                                   : fast_frag_mn<TN>(tb, wcol + j * 16, lane));
 
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const V8H4 ah = widen32(A_KMAJ ? fast_frag_k(ta, wm * 128 + i * 16, lane)
-                                           : fast_frag_mn<FM>(ta, wm * 128 + i * 16, lane));
-            const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sa[buf][wm * 128 + i * 16 + 4 * (lane >> 4)]);
+        for (int i = 0; i < IT; i++) {
+            const V8H4 ah = widen32(A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane)
+                                           : fast_frag_mn<TM>(ta, wrow + i * 16, lane));
+            const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sa[buf][wrow + i * 16 + 4 * (lane >> 4)]);
             const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
+            for (int j = 0; j < JT; j++) {
                 const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                 v4f P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[0], bh[j].c[0], zero, 0, 0, 0);
                 P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[1], bh[j].c[1], P, 0, 0, 0);
@@ -460,15 +488,18 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs p, int tiles
         }
     }
 
+    const int wrow = wm * IT * 16, wcol = wn * JT * 16;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < IT; i++)
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int64_t m = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + r;
+            const int64_t m = m0 + wrow + i * 16 + 4 * (lane >> 4) + r;
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
-                if (CBF16)
+            for (int j = 0; j < JT; j++) {
+                const int64_t n = n0 + wcol + j * 16 + (lane & 15);
+                if (OUT_PARTIAL)
+                    ws[((int64_t)split * p.M + m) * p.N + n] = acc[i][j][r];
+                else if (CBF16)
                     reinterpret_cast<uint16_t *>(p.C)[m * p.ldc + n] = to_bf16(acc[i][j][r]);
                 else
                     reinterpret_cast<float *>(p.C)[m * p.ldc + n] = acc[i][j][r];
@@ -476,41 +507,132 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs p, int tiles
         }
 }
 
-template <int LAYOUT, int BGRAN, bool CBF16>
-hipError_t launch_fast(const GemmArgs &a, hipStream_t st)
+// C[m][n] = sum over s = 0 .. splits-1, in that order, of ws[s][m][n]; four
+// consecutive columns per thread (N % 4 == 0 on this path).
+template <bool CBF16>
+__global__ __launch_bounds__(256) void gemm_split_reduce(const float *__restrict__ ws, int splits, int64_t M,
+                                                         int64_t N, void *__restrict__ C, int64_t ldc)
 {
-    const int tiles_m = (int)(a.M / FM), tiles_n = (int)(a.N / FN);
-    hipLaunchKernelGGL((gemm_fast_kernel<LAYOUT, BGRAN, CBF16>), dim3(tiles_m * tiles_n), dim3(256), 0,
-                       st, a, tiles_m, tiles_n);
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n4 = N / 4;
+    if (q >= M * n4)
+        return;
+    const int64_t m = q / n4, n = (q - m * n4) * 4;
+    float4 sum = *reinterpret_cast<const float4 *>(ws + m * N + n);
+    for (int s = 1; s < splits; s++) {
+        const float4 v = *reinterpret_cast<const float4 *>(ws + ((int64_t)s * M + m) * N + n);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+    }
+    if (CBF16) {
+        const uint32_t lo = (uint32_t)to_bf16(sum.x) | ((uint32_t)to_bf16(sum.y) << 16);
+        const uint32_t hi = (uint32_t)to_bf16(sum.z) | ((uint32_t)to_bf16(sum.w) << 16);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(C) + m * ldc + n) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(C) + m * ldc + n) = sum;
+    }
+}
+
+// Launch plan for an aligned problem: tile configuration and number of K splits.
+struct FastPlan {
+    bool ok;       // aligned fast path applies
+    bool large;    // CfgL (256 x 256) rather than CfgS (256 x 128)
+    int splits;    // K splits (1 = none)
+};
+
+constexpr int kComputeUnits = 256;
+
+FastPlan fast_plan(int64_t M, int64_t N, int64_t K)
+{
+    FastPlan best = {false, false, 1};
+    if (K <= 0 || K % 128 || M % CfgS::TM || N % CfgS::TN)
+        return best;
+    const int64_t KB = K / 128;
+    double best_cost = 1e300;
+    for (int large = 0; large < 2; large++) {
+        const int TM = large ? CfgL::TM : CfgS::TM, TN = large ? CfgL::TN : CfgS::TN;
+        if (M % TM || N % TN)
+            continue;
+        const int64_t tiles = (M / TM) * (N / TN);
+        for (int sp = 1; sp <= 8; sp *= 2) {
+            if (sp > 1 && KB / sp < 4)
+                break;
+            const int64_t rounds = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
+            // time in units of one 256 x 128 x 128 block step (about 2 us): rounds x steps x tile area
+            double cost = (double)rounds * (double)((KB + sp - 1) / sp) * (large ? 2.0 : 1.0) *
+                          (large ? 0.9 : 1.0);
+            if (sp > 1)   // partial sums written and re-read: (sp + 1) M N 4 bytes at ~4 TB/s
+                cost += (double)(sp + 1) * M * N * 4.0 / 4e12 / 2e-6;
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = {true, large != 0, sp};
+            }
+        }
+    }
+    return best;
+}
+
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_fast_cfg(const GemmArgs &a, int splits, float *ws, hipStream_t st)
+{
+    const int tiles_m = (int)(a.M / Cfg::TM), tiles_n = (int)(a.N / Cfg::TN);
+    const dim3 grid((unsigned)(tiles_m * tiles_n * splits));
+    if (splits == 1) {
+        hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, false>), grid, dim3(Cfg::THREADS), 0,
+                           st, a, tiles_m, tiles_n, 1, (float *)nullptr);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, true>), grid, dim3(Cfg::THREADS), 0, st,
+                       a, tiles_m, tiles_n, splits, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t quads = a.M * (a.N / 4);
+    hipLaunchKernelGGL((gemm_split_reduce<CBF16>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, ws,
+                       splits, a.M, a.N, a.C, a.ldc);
     return hipGetLastError();
 }
 
 template <int LAYOUT, int BGRAN, bool CBF16>
-hipError_t launch_one(const GemmArgs &a, hipStream_t st)
+hipError_t launch_fast(const GemmArgs &a, const FastPlan &plan, float *ws, hipStream_t st)
 {
-    if (a.M % FM == 0 && a.N % FN == 0 && a.K % 128 == 0 && a.K > 0)
-        return launch_fast<LAYOUT, BGRAN, CBF16>(a, st);
+    if (plan.large)
+        return launch_fast_cfg<CfgL, LAYOUT, BGRAN, CBF16>(a, plan.splits, ws, st);
+    return launch_fast_cfg<CfgS, LAYOUT, BGRAN, CBF16>(a, plan.splits, ws, st);
+}
+
+template <int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_one(const GemmArgs &a, float *ws, hipStream_t st)
+{
+    const FastPlan plan = fast_plan(a.M, a.N, a.K);
+    if (plan.ok)
+        return launch_fast<LAYOUT, BGRAN, CBF16>(a, plan, ws, st);
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
     hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 template <int LAYOUT>
-hipError_t launch_layout(const GemmProblem &p, const GemmArgs &a, hipStream_t st)
+hipError_t launch_layout(const GemmProblem &p, const GemmArgs &a, float *ws, hipStream_t st)
 {
     if (p.bgran)
-        return p.c_bf16 ? launch_one<LAYOUT, 1, true>(a, st) : launch_one<LAYOUT, 1, false>(a, st);
-    return p.c_bf16 ? launch_one<LAYOUT, 0, true>(a, st) : launch_one<LAYOUT, 0, false>(a, st);
+        return p.c_bf16 ? launch_one<LAYOUT, 1, true>(a, ws, st) : launch_one<LAYOUT, 1, false>(a, ws, st);
+    return p.c_bf16 ? launch_one<LAYOUT, 0, true>(a, ws, st) : launch_one<LAYOUT, 0, false>(a, ws, st);
 }
 
 } // namespace
 
-size_t gemm_workspace_bytes(const GemmProblem &)
+size_t gemm_workspace_bytes(const GemmProblem &p)
 {
-    return 0;
+    const FastPlan plan = fast_plan(p.M, p.N, p.K);
+    if (!plan.ok || plan.splits == 1)
+        return 0;
+    return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
 }
 
-hipError_t launch_gemm(const GemmProblem &p, void *, hipStream_t st)
+hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st)
 {
     if (p.M == 0 || p.N == 0)
         return hipSuccess;
@@ -528,10 +650,11 @@ hipError_t launch_gemm(const GemmProblem &p, void *, hipStream_t st)
     a.ldc = p.ldc;
     a.KB = (p.K + 127) / 128;
     a.NB = (p.N + 127) / 128;
+    float *ws = reinterpret_cast<float *>(workspace);
     switch (p.layout) {
-    case 0: return launch_layout<0>(p, a, st);
-    case 1: return launch_layout<1>(p, a, st);
-    default: return launch_layout<2>(p, a, st);
+    case 0: return launch_layout<0>(p, a, ws, st);
+    case 1: return launch_layout<1>(p, a, ws, st);
+    default: return launch_layout<2>(p, a, ws, st);
     }
 }
 

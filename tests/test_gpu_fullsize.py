@@ -1,0 +1,135 @@
+"""GPU parity at the workload's full sizes, in the launch configurations the
+benchmark uses, on sampled outputs.
+
+Inputs are the seeded host tensors of the Qwen3-1.7B layer shapes (8,192
+tokens; hidden 2,048, FFN 6,144, 16/8 heads) and of the outlier-stress
+down-projection shape (16,384 tokens).  The oracle quantises the same inputs
+(its codes and scales must equal the GPU's byte for byte over the whole
+tensors) and computes sampled output entries one by one.  Sampled entries
+must meet the per-element bound (KB + 4) 2^-23 sum|terms| (plus half a BF16
+ulp for BF16 outputs) and the sampled relative Frobenius error must be
+<= 2e-6.
+"""
+import numpy as np
+import pytest
+import torch
+
+import blockwise_fp8_gemm_amd as pf
+import oracle
+import synth
+from helpers import bf16_to_f64, first_mismatch, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = 3000
+
+
+def _same(dev_t, ref, what):
+    got = host(dev_t)
+    if got.dtype == np.float32:
+        got, ref = got.view(np.uint32), ref.view(np.uint32)
+    assert first_mismatch(got, ref) is None, (what, first_mismatch(got, ref))
+
+
+def _check_sampled(layout, bgran, ops, C, K, seed, out):
+    qa, sa, qb, sb = ops
+    M, N = C.shape
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, SAMPLES)
+    ns = rng.integers(0, N, SAMPLES)
+    ms[:4] = [0, 0, M - 1, M - 1]
+    ns[:4] = [0, N - 1, 0, N - 1]
+    ref = oracle.gemm_entries(layout, qa, sa, qb, sb, bgran, ms, ns)
+    ref_abs = oracle.gemm_entries(layout, qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), bgran, ms, ns)
+    E = ((K + 127) // 128 + 4) * 2.0 ** -23 * ref_abs
+    h = host(C)
+    got = bf16_to_f64(h[ms, ns]) if out == torch.bfloat16 else h[ms, ns].astype(np.float64)
+    tol = E + 2.0 ** -8 * (np.abs(ref) + E) if out == torch.bfloat16 else E
+    bad = np.flatnonzero(np.abs(got - ref) > tol)
+    assert bad.size == 0, ("entry", int(ms[bad[0]]), int(ns[bad[0]]), got[bad[0]], ref[bad[0]])
+    if out == torch.float32:
+        err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err <= 2e-6, err
+
+
+def _workspace(layout, M, N, K, bgran, dev):
+    n = pf.puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=dev), n
+
+
+LAYER = [(g, n, k) for g, n, k, _ in synth.LAYER_GEMMS if g in ("q", "k", "gate", "down")]
+
+
+@pytest.mark.parametrize("g,n_out,k_in", LAYER, ids=[x[0] for x in LAYER])
+def test_layer_gemm_full_size(dev, g, n_out, k_in):
+    """Forward, data gradient and weight gradient of one projection at 8,192 tokens."""
+    T = synth.TOKENS
+    j = [x[0] for x in synth.LAYER_GEMMS].index(g)
+    X = synth.normal((T, k_in), 1.0, synth.seed_of(2, 0, 100 + j), "bf16")
+    W = synth.normal((n_out, k_in), 0.02, synth.seed_of(2, 0, 110 + j))
+    dY = synth.normal((T, n_out), 1e-3, synth.seed_of(3, 0, 120 + j), "bf16")
+    dX_, dW_, ddY = to_dev(X), to_dev(W), to_dev(dY)
+
+    rqx, rsx = oracle.quant_act(X)
+    rqw, rsw = oracle.quant_weight(W)
+    rqd, rsd = oracle.quant_act(dY)
+    rqdt, rsdt = oracle.quant_transpose(dY, True)
+    rqxt, rsxt = oracle.quant_transpose(X, True)
+
+    qx, sx = pf.puro_fp8_quant_act(dX_)
+    qw, sw = pf.puro_fp8_quant_weight(dW_)
+    qd, sd = pf.puro_fp8_quant_act(ddY)
+    qdt, sdt = pf.puro_fp8_quant_transpose(ddY, True)
+    qxt, sxt = pf.puro_fp8_quant_transpose(dX_, True)
+    torch.cuda.synchronize()
+    for t, r, w in ((qx, rqx, "qX"), (sx, rsx, "sX"), (qw, rqw, "qW"), (sw, rsw, "sW"), (qd, rqd, "qdY"),
+                    (sd, rsd, "sdY"), (qdt, rqdt, "qdYt"), (sdt, rsdt, "sdYt"), (qxt, rqxt, "qXt"),
+                    (sxt, rsxt, "sXt")):
+        _same(t, r, w)
+
+    ws, nws = _workspace("NT", T, n_out, k_in, "128x128", dev)
+    Y = pf.puro_fp8_gemm("NT", qx, sx, qw, sw, "128x128", torch.bfloat16, workspace=ws if nws else None)
+    ws, nws = _workspace("NN", T, k_in, n_out, "128x128", dev)
+    dXg = pf.puro_fp8_gemm("NN", qd, sd, qw, sw, "128x128", torch.bfloat16, workspace=ws if nws else None)
+    ws, nws = _workspace("NT", n_out, k_in, T, "1x128", dev)
+    dWg = pf.puro_fp8_gemm("NT", qdt, sdt, qxt, sxt, "1x128", torch.float32, workspace=ws if nws else None)
+    torch.cuda.synchronize()
+    _check_sampled("NT", "128x128", (rqx, rsx, rqw, rsw), Y, k_in, 1, torch.bfloat16)
+    _check_sampled("NN", "128x128", (rqd, rsd, rqw, rsw), dXg, n_out, 2, torch.bfloat16)
+    _check_sampled("NT", "1x128", (rqdt, rsdt, rqxt, rsxt), dWg, T, 3, torch.float32)
+
+
+def test_outlier_stress_full_size(dev):
+    """Down-projection shape at 16,384 tokens: 1% of channels x100, lognormal gradients,
+    all-zero 128-blocks; forward, data gradient, weight gradient (FP32 outputs)."""
+    T, K_in, N_out = 16384, 6144, 2048
+    X, _ = synth.outlier_activations(T, K_in, synth.seed_of(5, 0, 0))
+    dY = synth.lognormal_gradients(T, N_out, synth.seed_of(5, 0, 1))
+    W = synth.normal((N_out, K_in), 0.02, synth.seed_of(5, 0, 2))
+    dX_, dW_, ddY = to_dev(X), to_dev(W), to_dev(dY)
+    rqx, rsx = oracle.quant_act(X)
+    rqw, rsw = oracle.quant_weight(W)
+    rqd, rsd = oracle.quant_act(dY)
+    rqdt, rsdt = oracle.quant_transpose(dY, True)
+    rqxt, rsxt = oracle.quant_transpose(X, True)
+    assert (rsx == 0).any() and (rsdt == 0).any()
+    qx, sx = pf.puro_fp8_quant_act(dX_)
+    qw, sw = pf.puro_fp8_quant_weight(dW_)
+    qd, sd = pf.puro_fp8_quant_act(ddY)
+    qdt, sdt = pf.puro_fp8_quant_transpose(ddY, True)
+    qxt, sxt = pf.puro_fp8_quant_transpose(dX_, True)
+    torch.cuda.synchronize()
+    for t, r, w in ((qx, rqx, "qX"), (sx, rsx, "sX"), (qw, rqw, "qW"), (qd, rqd, "qdY"), (sd, rsd, "sdY"),
+                    (qdt, rqdt, "qdYt"), (sdt, rsdt, "sdYt"), (qxt, rqxt, "qXt"), (sxt, rsxt, "sXt")):
+        _same(t, r, w)
+    outs = []
+    for layout, A, sA, B, sB, bg, K in (("NT", qx, sx, qw, sw, "128x128", K_in),
+                                        ("NN", qd, sd, qw, sw, "128x128", N_out),
+                                        ("NT", qdt, sdt, qxt, sxt, "1x128", T)):
+        M, N, _ = pf.gemm_dims(layout, A, B)
+        ws, nws = _workspace(layout, M, N, K, bg, dev)
+        outs.append(pf.puro_fp8_gemm(layout, A, sA, B, sB, bg, torch.float32, workspace=ws if nws else None))
+    torch.cuda.synchronize()
+    _check_sampled("NT", "128x128", (rqx, rsx, rqw, rsw), outs[0], K_in, 4, torch.float32)
+    _check_sampled("NN", "128x128", (rqd, rsd, rqw, rsw), outs[1], N_out, 5, torch.float32)
+    _check_sampled("NT", "1x128", (rqdt, rsdt, rqxt, rsxt), outs[2], T, 6, torch.float32)

@@ -98,6 +98,8 @@ SHAPES = [
     ("ragged", 200, 136, 300),
     ("ragged_thin", 130, 7, 1000),
     ("k_tail_only", 128, 128, 200),
+    ("split_k", 256, 128, 2048),
+    ("split_k_wide", 256, 256, 4096),
 ]
 
 
