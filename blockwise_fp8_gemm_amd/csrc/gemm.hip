@@ -353,18 +353,21 @@ __device__ __forceinline__ V8H4 widen32(const v8i &f)
     return h;
 }
 
-template <int WM_, int WN_, int IT_, int JT_>
+template <int WM_, int WN_, int IT_, int JT_, int STAGES_>
 struct FastCfg {
-    static constexpr int WM = WM_, WN = WN_, IT = IT_, JT = JT_;
+    static constexpr int WM = WM_, WN = WN_, IT = IT_, JT = JT_, STAGES = STAGES_;
     static constexpr int NW = WM * WN, THREADS = 64 * NW;
     static constexpr int TM = WM * IT * 16, TN = WN * JT * 16;
     static constexpr int A_BYTES = TM * 128, B_BYTES = TN * 128;
+    // direct copies each wave issues per K block: A and B tiles in 1 KB
+    // pieces, plus one 4-byte-per-lane copy for the block's scales
+    static constexpr int LOADS = TM / 8 / NW + TN / 8 / NW + 1;
 };
 
-// 256 x 256 workgroup tiles (8 waves of 128 x 64) for large outputs, 256 x 128
-// (8 waves of 64 x 64) where 256 x 256 would leave compute units idle.
-typedef FastCfg<2, 4, 8, 4> CfgL;
-typedef FastCfg<4, 2, 4, 4> CfgS;
+// 256 x 256 workgroup tiles (8 waves of 128 x 64, two LDS stages) and
+// 256 x 128 tiles (8 waves of 64 x 64, three LDS stages).
+typedef FastCfg<2, 4, 8, 4, 2> CfgL;
+typedef FastCfg<4, 2, 4, 4, 3> CfgS;
 
 // Split-K: workgroup b handles K blocks [kb_lo, kb_hi) of split s = b / tiles
 // and, with OUT_PARTIAL, stores FP32 partial sums to ws[s][M][N] (row stride N)
@@ -378,9 +381,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int
     constexpr int NW = Cfg::NW, TM = Cfg::TM, TN = Cfg::TN, IT = Cfg::IT, JT = Cfg::JT;
     constexpr int A_BYTES = Cfg::A_BYTES, B_BYTES = Cfg::B_BYTES;
     static_assert(TN % 128 == 0 || !BGRAN || TN <= 128, "tile columns within 128-wide weight tiles");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][A_BYTES + B_BYTES];
-    __shared__ __attribute__((aligned(16))) float lds_sa[2][TM];
-    __shared__ __attribute__((aligned(16))) float lds_sb[2][TN];
+    constexpr int STAGES = Cfg::STAGES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES][A_BYTES + B_BYTES];
+    // per stage: A scales [0, TM), B scales from TM on, then unused slots
+    __shared__ __attribute__((aligned(16))) float lds_sc[STAGES][NW * 64];
+    static_assert(TM + TN <= NW * 64, "one scale slot per lane");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
@@ -425,42 +430,61 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int
             fast_stage_k<TN, NW>(tb, p.B, p.ldb, n0, k0, wave, lane);
         else
             fast_stage_mn<TN, NW>(tb, p.B, p.ldb, k0, n0, wave, lane);
-        if (tid < TM) {   // scales of A: one 4-byte direct load per row
+        // Scales: lane q of the workgroup copies A's scale of row q (q < TM),
+        // then B's scales (one per column, or one per 128-wide weight tile),
+        // and a harmless duplicate of A's first scale beyond that, so that
+        // every wave issues the same copies.
+        const int nsb = BGRAN ? TN / 128 : TN;
+        const float *src;
+        if (tid < TM) {
             const int64_t m = m0 + tid;
-            load_lds4(A_KMAJ ? (const void *)(p.sA + m * p.KB + kb) : (const void *)(p.sA + kb * p.M + m),
-                      &lds_sa[buf][wave * 64]);
+            src = A_KMAJ ? p.sA + m * p.KB + kb : p.sA + kb * p.M + m;
+        } else if (tid < TM + nsb) {
+            const int64_t q = tid - TM;
+            if (BGRAN) {
+                const int64_t nb = (n0 >> 7) + q;
+                src = B_KMAJ ? p.sB + nb * p.KB + kb : p.sB + kb * p.NB + nb;
+            } else {
+                const int64_t n = n0 + q;
+                src = B_KMAJ ? p.sB + n * p.KB + kb : p.sB + kb * p.N + n;
+            }
+        } else {
+            src = A_KMAJ ? p.sA + m0 * p.KB + kb : p.sA + kb * p.M + m0;
         }
-        if (!BGRAN && tid < TN) {
-            const int64_t n = n0 + tid;
-            load_lds4(B_KMAJ ? (const void *)(p.sB + n * p.KB + kb) : (const void *)(p.sB + kb * p.N + n),
-                      &lds_sb[buf][wave * 64]);
-        }
+        load_lds4(src, &lds_sc[buf][wave * 64]);
     };
 
-    stage(kb_lo, 0);
+    // vmcnt(n) immediate for gfx9-family s_waitcnt (expcnt and lgkmcnt left unconstrained)
+    constexpr int WAIT_NEWEST = 0x0F70 | (Cfg::LOADS & 15) | ((Cfg::LOADS >> 4) << 14);
+    static_assert(Cfg::LOADS < 64, "vmcnt range");
+
+    for (int s = 0; s < STAGES - 1; s++)
+        if (kb_lo + s < kb_hi)
+            stage(kb_lo + s, s);
+    int buf = 0;
     for (int64_t kb = kb_lo; kb < kb_hi; kb++) {
-        const int buf = (int)((kb - kb_lo) & 1);
-        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of block kb have landed
-        __syncthreads();                 // ... and everyone's; block kb-1 is no longer read
-        if (kb + 1 < kb_hi)
-            stage(kb + 1, buf ^ 1);
+        // Block kb's copies must have landed.  With three stages, block
+        // kb+1's copies (issued one iteration later) may still be in flight.
+        if (STAGES > 2 && kb + 1 < kb_hi)
+            __builtin_amdgcn_s_waitcnt(WAIT_NEWEST);
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   // everyone's copies of block kb have landed; block kb-1 is no longer read
+        if (kb + STAGES - 1 < kb_hi) {
+            int nb_ = buf + STAGES - 1;
+            if (nb_ >= STAGES)
+                nb_ -= STAGES;
+            stage(kb + STAGES - 1, nb_);
+        }
 
         const uint8_t *ta = lds[buf];
         const uint8_t *tb = lds[buf] + A_BYTES;
         const int wrow = wm * IT * 16, wcol = wn * JT * 16;
 
         float sbv[JT];
-        if (BGRAN) {
 #pragma unroll
-            for (int j = 0; j < JT; j++) {
-                const int64_t nb = (n0 + wcol + j * 16) >> 7;
-                sbv[j] = B_KMAJ ? p.sB[nb * p.KB + kb] : p.sB[kb * p.NB + nb];
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < JT; j++)
-                sbv[j] = lds_sb[buf][wcol + j * 16 + (lane & 15)];
-        }
+        for (int j = 0; j < JT; j++)
+            sbv[j] = BGRAN ? lds_sc[buf][TM + ((wcol + j * 16) >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)];
 
         V8H4 bh[JT];
 #pragma unroll
@@ -468,24 +492,56 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int
             bh[j] = widen32(B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane)
                                    : fast_frag_mn<TN>(tb, wcol + j * 16, lane));
 
+        // A is widened one K sub-step (8 values per lane) at a time, right
+        // before its MFMAs, and the next row block's fragment is read as soon
+        // as the last sub-step of this one is widened; each sub-step runs over
+        // all JT tiles so that no MFMA waits on the one just issued.  Larger
+        // wave tiles (not INTERLEAVE) have no registers to spare for that:
+        // each row block is read and widened whole, and each tile's four
+        // MFMAs run back to back with one partial live.
+        constexpr bool INTERLEAVE = IT * JT <= 16;
+        v8i araw = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
 #pragma unroll
         for (int i = 0; i < IT; i++) {
-            const V8H4 ah = widen32(A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane)
-                                           : fast_frag_mn<TM>(ta, wrow + i * 16, lane));
-            const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sa[buf][wrow + i * 16 + 4 * (lane >> 4)]);
+            const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sc[buf][wrow + i * 16 + 4 * (lane >> 4)]);
             const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+            if (INTERLEAVE) {
+                v4f P[JT];
 #pragma unroll
-            for (int j = 0; j < JT; j++) {
-                const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                v4f P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[0], bh[j].c[0], zero, 0, 0, 0);
-                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[1], bh[j].c[1], P, 0, 0, 0);
-                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[2], bh[j].c[2], P, 0, 0, 0);
-                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[3], bh[j].c[3], P, 0, 0, 0);
+                for (int q = 0; q < 4; q++) {
+                    const v8h aq = widen8(araw, q);
+                    if (q == 3 && i + 1 < IT)
+                        araw = A_KMAJ ? fast_frag_k(ta, wrow + (i + 1) * 16, lane)
+                                      : fast_frag_mn<TM>(ta, wrow + (i + 1) * 16, lane);
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    acc[i][j][r] = fmaf(sa[r] * sbv[j], P[r], acc[i][j][r]);
+                    for (int j = 0; j < JT; j++) {
+                        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                        P[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bh[j].c[q], q ? P[j] : zero, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < JT; j++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[i][j][r] = fmaf(sa[r] * sbv[j], P[j][r], acc[i][j][r]);
+            } else {
+                if (i > 0)
+                    araw = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
+                const V8H4 ah = widen32(araw);
+#pragma unroll
+                for (int j = 0; j < JT; j++) {
+                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    v4f P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[0], bh[j].c[0], zero, 0, 0, 0);
+#pragma unroll
+                    for (int q = 1; q < 4; q++)
+                        P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[q], bh[j].c[q], P, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[i][j][r] = fmaf(sa[r] * sbv[j], P[r], acc[i][j][r]);
+                }
             }
         }
+        buf = (buf + 1 == STAGES) ? 0 : buf + 1;
     }
 
     const int wrow = wm * IT * 16, wcol = wn * JT * 16;
