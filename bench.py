@@ -3,9 +3,10 @@
 One step = one micro-batch (2 x 4,096 = 8,192 tokens) through the linear
 layers of all 28 Transformer layers: the seven unfused projections
 (q, k, v, o, gate, up, down) in forward (Y = X W^T), data gradient
-(dX = dY W) and weight gradient (dW = dY^T X), with every quantiser
-(activations 1x128, weights 128x128, gradients 1x128, token-dimension copies
-for the weight gradient) inside the timed region.  Shapes come from the
+(dX = dY W) and weight gradient (dW = dY^T X), with every quantiser inside
+the timed region: weights in 128x128 tiles, and each layer input X and each
+output gradient dY quantised both ways in one read (1x128 along features for
+the forward / data-gradient GEMM, 128-token blocks for the weight gradient).  Shapes come from the
 Puro-2B-Base model card (Qwen3-1.7B configuration: hidden 2,048, FFN 6,144,
 16 / 8 heads, 28 layers; sequence length 4,096, micro-batch 2).
 
@@ -105,32 +106,28 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
         dys = {g: synth.device_normal((T, n), 1e-3, synth.seed_of(4, layer, 20 + j), "bf16", dev)
                for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
         keep += [xs, wts, dys]
-        # forward: quantise each distinct input once, each weight once, then Y = X W^T
+        # forward: each distinct input quantised once, both ways (the token-blocked
+        # copy is kept for the weight gradient); each weight once; Y = X W^T
         for name, c in synth.LAYER_INPUTS:
-            plan.add(L.puro_fp8_quant_act, (P(xs[name]), BF16, T, c, c, P(qx[name]), c, P(sx[name]),
-                                            stream_ptr), "quant_act", "quant_act", 0, T * c * (2 + 1 + 4 / 128))
+            plan.add(L.puro_fp8_quant_dual, (P(xs[name]), BF16, T, c, c, P(qx[name]), c, P(sx[name]), 1,
+                                             P(qxt[name]), T, P(sxt[name]), stream_ptr),
+                     "quant_dual", "quant_dual", 0, T * c * (2 + 2 + 8 / 128))
         for g, n, k, src in synth.LAYER_GEMMS:
             plan.add(L.puro_fp8_quant_weight, (P(wts[g]), F32, n, k, k, P(qw[g]), k, P(sw[g]), stream_ptr),
                      "quant_weight", "quant_weight", 0, n * k * (4 + 1) + nb(n) * nb(k) * 4)
             plan.add(L.puro_fp8_gemm, (NT, T, n, k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]),
                                        S128, P(y[g]), BF16, n, WS, WSB, stream_ptr),
                      "gemm", "gemm_fwd_NT_128x128_bf16", 2.0 * T * n * k)
-        # data gradient: dX = dY W with the forward's quantised W
+        # backward, per projection: dY quantised both ways in one read, then the
+        # data gradient dX = dY W (the forward's quantised W) and the weight
+        # gradient dW = dY^T X (token-blocked copies)
         for g, n, k, src in synth.LAYER_GEMMS:
-            plan.add(L.puro_fp8_quant_act, (P(dys[g]), BF16, T, n, n, P(qdy), n, P(sdy), stream_ptr),
-                     "quant_act", "quant_act", 0, T * n * (2 + 1 + 4 / 128))
+            plan.add(L.puro_fp8_quant_dual, (P(dys[g]), BF16, T, n, n, P(qdy), n, P(sdy), 1, P(qdyt), T,
+                                             P(sdyt), stream_ptr),
+                     "quant_dual", "quant_dual", 0, T * n * (2 + 2 + 8 / 128))
             plan.add(L.puro_fp8_gemm, (NN, T, k, n, P(qdy), n, P(sdy), P(qw[g]), k, P(sw[g]), S128,
                                        P(dx[g]), BF16, k, WS, WSB, stream_ptr),
                      "gemm", "gemm_dgrad_NN_128x128_bf16", 2.0 * T * n * k)
-        # weight gradient: dW = dY^T X on token-blocked copies
-        for name, c in synth.LAYER_INPUTS:
-            plan.add(L.puro_fp8_quant_transpose, (P(xs[name]), BF16, T, c, c, 1, P(qxt[name]), T,
-                                                  P(sxt[name]), stream_ptr),
-                     "quant_transpose", "quant_transpose", 0, T * c * (2 + 1 + 4 / 128))
-        for g, n, k, src in synth.LAYER_GEMMS:
-            plan.add(L.puro_fp8_quant_transpose, (P(dys[g]), BF16, T, n, n, 1, P(qdyt), T, P(sdyt),
-                                                  stream_ptr),
-                     "quant_transpose", "quant_transpose", 0, T * n * (2 + 1 + 4 / 128))
             plan.add(L.puro_fp8_gemm, (NT, n, k, T, P(qdyt), T, P(sdyt), P(qxt[src]), T, P(sxt[src]),
                                        S1, P(dw[g]), F32, k, WS, WSB, stream_ptr),
                      "gemm", "gemm_wgrad_NT_1x128_f32", 2.0 * T * n * k)

@@ -9,6 +9,7 @@ Names mirror the C entry points:
     puro_fp8_quant_act(x)                 -> (q, s)   1x128 blocks along rows
     puro_fp8_quant_weight(w)              -> (q, s)   128x128 tiles
     puro_fp8_quant_transpose(x, t_out)    -> (q, s)   128-token blocks per column
+    puro_fp8_quant_dual(x, t_out)         -> both of the above from one read of x
     puro_fp8_gemm(layout, A, sA, B, sB, bgran, out_dtype) -> C
     puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
     puro_status_string(status)
@@ -52,6 +53,8 @@ def lib():
             f.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
         L.puro_fp8_quant_transpose.restype = i32
         L.puro_fp8_quant_transpose.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
+        L.puro_fp8_quant_dual.restype = i32
+        L.puro_fp8_quant_dual.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp, vp]
         L.puro_fp8_gemm_workspace_size.restype = ctypes.c_size_t
         L.puro_fp8_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i32]
         L.puro_fp8_gemm.restype = i32
@@ -182,6 +185,32 @@ def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None)
                                           1 if transpose_out else 0, _ptr(q), _ld(q), _ptr(s),
                                           _stream(stream)), "puro_fp8_quant_transpose")
     return q, s
+
+
+def puro_fp8_quant_dual(x, transpose_out=True, q_row=None, s_row=None, q_tok=None, s_tok=None,
+                        stream=None):
+    """One read of x [tokens][cols]: the outputs of puro_fp8_quant_act(x) and of
+    puro_fp8_quant_transpose(x, transpose_out).  Returns (q_row, s_row, q_tok, s_tok)."""
+    tokens, cols = x.shape
+    if q_row is None:
+        q_row = empty_2d(tokens, cols, torch.uint8, x.device)
+    if s_row is None:
+        s_row = torch.empty((tokens, _nblk(cols)), dtype=torch.float32, device=x.device)
+    qshape = (cols, tokens) if transpose_out else (tokens, cols)
+    sshape = (cols, _nblk(tokens)) if transpose_out else (_nblk(tokens), cols)
+    if q_tok is None:
+        q_tok = empty_2d(qshape[0], qshape[1], torch.uint8, x.device)
+    if s_tok is None:
+        s_tok = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    _need(q_row, (tokens, cols), torch.uint8, "q_row")
+    _need_dense(s_row, (tokens, _nblk(cols)), "s_row")
+    _need(q_tok, qshape, torch.uint8, "q_tok")
+    _need_dense(s_tok, sshape, "s_tok")
+    _check(lib().puro_fp8_quant_dual(_ptr(x), _dtype_code(x), tokens, cols, _ld(x), _ptr(q_row),
+                                     _ld(q_row), _ptr(s_row), 1 if transpose_out else 0,
+                                     _ptr(q_tok), _ld(q_tok), _ptr(s_tok), _stream(stream)),
+           "puro_fp8_quant_dual")
+    return q_row, s_row, q_tok, s_tok
 
 
 def gemm_dims(layout, A, B):

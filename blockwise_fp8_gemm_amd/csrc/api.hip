@@ -106,6 +106,31 @@ puro_status_t puro_fp8_quant_transpose(const void *x, puro_dtype_t xdt, int64_t 
     }
 }
 
+puro_status_t puro_fp8_quant_dual(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                  int64_t ldx, uint8_t *q_row, int64_t ldq_row, float *s_row,
+                                  int transpose_out, uint8_t *q_tok, int64_t ldq_tok, float *s_tok,
+                                  hipStream_t stream)
+{
+    try {
+        if (transpose_out != 0 && transpose_out != 1)
+            return PURO_ERR_ENUM;
+        puro_status_t st = check_quant(x, xdt, tokens, cols, ldx, q_row, ldq_row, cols, s_row);
+        if (st != PURO_OK)
+            return st;
+        st = check_quant(x, xdt, tokens, cols, ldx, q_tok, ldq_tok, transpose_out ? tokens : cols,
+                         s_tok);
+        if (st != PURO_OK)
+            return st;
+        if (tokens == 0 || cols == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_quant_dual(x, xdt == PURO_BF16, tokens, cols, ldx, q_row,
+                                                ldq_row, s_row, transpose_out == 1, q_tok, ldq_tok,
+                                                s_tok, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
 static puro_status_t check_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
                                 const uint8_t *A, int64_t lda, const float *sA, const uint8_t *B,
                                 int64_t ldb, const float *sB, puro_bscale_t bgran, const void *C,

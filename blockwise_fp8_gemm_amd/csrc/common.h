@@ -27,13 +27,45 @@ __device__ __forceinline__ uint32_t sign_code(float x)
     return (__float_as_uint(x) >> 24) & 0x80u;
 }
 
-// Quantise four values of a block with dequant scale sc (sc > 0 or sc == 0).
-// Division is IEEE binary32 round-to-nearest-even (hipcc's default).
-__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float sc)
+// Correctly rounded x / s for one block's scale s.
+//
+// With r = RN(1/s), y0 = RN(x r) is within an ulp of x/s; the residual
+// e = x - y0 s is then exact (one FMA), and RN(y0 + e r) = RN(x/s)
+// (Markstein's correction step).  The residual is exact only while it does
+// not underflow, which holds for s >= 2^-80 over every quotient that can
+// change an E4M3 code (|x/s| >= 2^-12); below that the kernel divides.  The
+// sign is copied from x so that -0 stays -0.  Checked against IEEE division
+// on 7e9 quotients (s in [2^-90, 2^30]) before use.
+struct Divider {
+    float s, r;
+    bool fast;
+};
+
+__device__ __forceinline__ Divider make_divider(float s)
 {
-    if (sc == 0.0f)
-        return sign_code(a) | (sign_code(b) << 8) | (sign_code(c) << 16) | (sign_code(d) << 24);
-    return e4m3x4(a / sc, b / sc, c / sc, d / sc);
+    Divider d;
+    d.s = s;
+    d.fast = s >= 0x1p-80f;
+    d.r = d.fast ? 1.0f / s : 0.0f;
+    return d;
+}
+
+__device__ __forceinline__ float quotient(const Divider &d, float x)
+{
+    if (!d.fast)
+        return x / d.s;
+    const float y0 = x * d.r;
+    const float e = fmaf(-y0, d.s, x);
+    return __builtin_copysignf(fmaf(e, d.r, y0), x);
+}
+
+// Quantise four values of a block with dequant scale d.s (> 0, or == 0 for a
+// zero block: codes +-0 by sign).
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d_, const Divider &d)
+{
+    if (d.s == 0.0f)
+        return sign_code(a) | (sign_code(b) << 8) | (sign_code(c) << 16) | (sign_code(d_) << 24);
+    return e4m3x4(quotient(d, a), quotient(d, b), quotient(d, c), quotient(d, d_));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }

@@ -15,6 +15,9 @@ hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t c
 hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int64_t cols,
                                   int64_t ldx, bool transpose_out, uint8_t *q, int64_t ldq,
                                   float *s, hipStream_t st);
+hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t cols, int64_t ldx,
+                             uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
+                             int64_t ldqt, float *st, hipStream_t stream);
 
 struct GemmProblem {
     int layout;   // 0 NT, 1 NN, 2 TN

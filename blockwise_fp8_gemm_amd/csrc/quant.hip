@@ -18,78 +18,95 @@
 namespace puro {
 
 // ---------------------------------------------------------------------------
-// 1x128 row blocks.  One 16-lane group per block, 8 consecutive elements per
-// lane (one 16-byte load for BF16, two for FP32), amax by cross-lane max.
+// 1x128 row blocks.  One 16-lane group per run of BPG consecutive blocks of a
+// row, 8 consecutive elements of each block per lane (one 16-byte load for
+// BF16, two for FP32); all of a lane's loads are issued before any arithmetic
+// so that each wave keeps BPG KB (BF16) in flight.  amax by cross-lane max
+// within the 16-lane group.
 // ---------------------------------------------------------------------------
+constexpr int BPG = 4;
+
 template <typename T>
 __global__ __launch_bounds__(256) void quant_act_kernel(const T *__restrict__ x, int64_t rows,
                                                         int64_t cols, int64_t ldx,
                                                         uint8_t *__restrict__ q, int64_t ldq,
                                                         float *__restrict__ s, int64_t nb)
 {
-    const int64_t blk = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
-    if (blk >= rows * nb)
+    const int64_t runs = (nb + BPG - 1) / BPG;
+    const int64_t grp = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    if (grp >= rows * runs)
         return;  // whole 16-lane groups leave together
     const int l16 = threadIdx.x & 15;
-    const int64_t r = blk / nb;
-    const int64_t b = blk - r * nb;
-    const int64_t c0 = b * 128 + l16 * 8;
-    const bool full = (b * 128 + 128 <= cols);
+    const int64_t r = grp / runs;
+    const int64_t b0 = (grp - r * runs) * BPG;
     const T *xr = x + r * ldx;
 
-    float v[8];
-    if (full) {
-        Elem<T>::load8(xr + c0, v);
-    } else {
+    float v[BPG][8];
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            v[i] = (c0 + i < cols) ? Elem<T>::load(xr + c0 + i) : 0.0f;
+    for (int u = 0; u < BPG; u++) {
+        const int64_t c0 = (b0 + u) * 128 + l16 * 8;
+        if (c0 + 8 <= cols) {
+            Elem<T>::load8(xr + c0, v[u]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                v[u][i] = (c0 + i < cols) ? Elem<T>::load(xr + c0 + i) : 0.0f;
+        }
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    const float sc = amax / 448.0f;
-
-    const uint32_t lo = quant4(v[0], v[1], v[2], v[3], sc);
-    const uint32_t hi = quant4(v[4], v[5], v[6], v[7], sc);
     uint8_t *qr = q + r * ldq;
-    if (full) {
-        *reinterpret_cast<uint2 *>(qr + c0) = make_uint2(lo, hi);
-    } else {
+#pragma unroll
+    for (int u = 0; u < BPG; u++) {
+        const int64_t b = b0 + u;
+        if (b >= nb)
+            break;
+        float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            if (c0 + i < cols)
-                qr[c0 + i] = (uint8_t)(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFF);
+            amax = fmaxf(amax, fabsf(v[u][i]));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+        const float sc = amax / 448.0f;
+        const Divider dv = make_divider(sc);
+        const uint32_t lo = quant4(v[u][0], v[u][1], v[u][2], v[u][3], dv);
+        const uint32_t hi = quant4(v[u][4], v[u][5], v[u][6], v[u][7], dv);
+        const int64_t c0 = b * 128 + l16 * 8;
+        if (c0 + 8 <= cols) {
+            *reinterpret_cast<uint2 *>(qr + c0) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (c0 + i < cols)
+                    qr[c0 + i] = (uint8_t)(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFF);
+        }
+        if (l16 == 0)
+            s[r * nb + b] = sc;
     }
-    if (l16 == 0)
-        s[r * nb + b] = sc;
 }
 
 // ---------------------------------------------------------------------------
-// 128x128 weight tiles.  One workgroup per tile; thread t owns columns
-// 8*(t%16) .. +7 of rows t/16 + 16 i (i = 0..7): 64 values in registers.
+// 128x128 weight tiles.  One 1024-thread workgroup per tile (weights have few
+// tiles, so many threads per tile keep the GPU busy); thread t owns columns
+// 8*(t%16) .. +7 of rows t/16 and t/16 + 64: 16 values in registers.  amax:
+// cross-lane max per wave, then across the 16 waves through LDS.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void quant_weight_kernel(const T *__restrict__ w, int64_t rows,
-                                                           int64_t cols, int64_t ldw,
-                                                           uint8_t *__restrict__ q, int64_t ldq,
-                                                           float *__restrict__ s, int64_t cb)
+__global__ __launch_bounds__(1024) void quant_weight_kernel(const T *__restrict__ w, int64_t rows,
+                                                            int64_t cols, int64_t ldw,
+                                                            uint8_t *__restrict__ q, int64_t ldq,
+                                                            float *__restrict__ s, int64_t cb)
 {
-    __shared__ float red[4];
+    __shared__ float red[16];
     const int t = threadIdx.x;
     const int cc = t & 15, rg = t >> 4;
     const int64_t r0 = (int64_t)blockIdx.y * 128, cbase = (int64_t)blockIdx.x * 128;
     const int64_t c0 = cbase + cc * 8;
     const bool full_tile = (r0 + 128 <= rows) && (cbase + 128 <= cols);
 
-    float v[8][8];
+    float v[2][8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int64_t r = r0 + rg + 16 * i;
+    for (int i = 0; i < 2; i++) {
+        const int64_t r = r0 + rg + 64 * i;
         const T *wr = w + r * ldw;
         if (full_tile) {
             Elem<T>::load8(wr + c0, v[i]);
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const T *__restrict__
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 8; j++)
             amax = fmaxf(amax, fabsf(v[i][j]));
@@ -111,14 +128,18 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const T *__restrict__
     if ((t & 63) == 0)
         red[t >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    amax = red[0];
+#pragma unroll
+    for (int i = 1; i < 16; i++)
+        amax = fmaxf(amax, red[i]);
     const float sc = amax / 448.0f;
+    const Divider dv = make_divider(sc);
 
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int64_t r = r0 + rg + 16 * i;
-        const uint32_t lo = quant4(v[i][0], v[i][1], v[i][2], v[i][3], sc);
-        const uint32_t hi = quant4(v[i][4], v[i][5], v[i][6], v[i][7], sc);
+    for (int i = 0; i < 2; i++) {
+        const int64_t r = r0 + rg + 64 * i;
+        const uint32_t lo = quant4(v[i][0], v[i][1], v[i][2], v[i][3], dv);
+        const uint32_t hi = quant4(v[i][4], v[i][5], v[i][6], v[i][7], dv);
         uint8_t *qr = q + r * ldq;
         if (full_tile) {
             *reinterpret_cast<uint2 *>(qr + c0) = make_uint2(lo, hi);
@@ -135,10 +156,11 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const T *__restrict__
 
 // ---------------------------------------------------------------------------
 // Token blocks (128 tokens x 1 column), for a tile of 128 tokens x 64 columns
-// per workgroup.  Thread t owns columns 8*(t%8) .. +7 of tokens t/8 + 32 i
-// (i = 0..3).  Column amax: per-thread max over its 4 tokens, cross-lane max
-// over lanes with equal t%8, then across the 4 waves through LDS.  The
-// transposed output is assembled in LDS and written as 128-byte rows.
+// per workgroup.  Thread t owns columns 8*(t%8) .. +7 of the 4 consecutive
+// tokens 4*(t/8) .. +3.  Column amax: per-thread max over its 4 tokens,
+// cross-lane max over lanes with equal t%8, then across the 4 waves through
+// LDS.  For the transposed output each thread packs its 4 token codes of a
+// column into one 32-bit LDS word; the tile is written out as 128-byte rows.
 // ---------------------------------------------------------------------------
 template <typename T, bool TRANSPOSE_OUT>
 __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restrict__ x,
@@ -149,10 +171,10 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
 {
     __shared__ float red[4][64];
     __shared__ float scl[64];
-    __shared__ __attribute__((aligned(16))) uint8_t tile[64][128 + 16];
+    __shared__ uint32_t tile[64][32 + 1];   // [column][token/4], odd stride: no bank conflicts
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int cc = t & 7, rr = t >> 3;
+    const int cc = t & 7, rq = t >> 3;
     const int64_t tok0 = (int64_t)blockIdx.y * 128;
     const int64_t col0 = (int64_t)blockIdx.x * 64;
     const int64_t c0 = col0 + cc * 8;
@@ -161,7 +183,7 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
     float v[4][8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int64_t tk = tok0 + rr + 32 * i;
+        const int64_t tk = tok0 + 4 * rq + i;
         const T *xr = x + tk * ldx;
         if (full) {
             Elem<T>::load8(xr + c0, v[i]);
@@ -199,41 +221,14 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
     }
     __syncthreads();
 
-    float scj[8];
+    uint32_t word[8];   // word[j]: the 4 token codes of column cc*8+j
 #pragma unroll
     for (int j = 0; j < 8; j++)
-        scj[j] = scl[cc * 8 + j];
-
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        uint32_t code[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float sc = scj[j];
-            code[j] = (sc == 0.0f) ? sign_code(v[i][j])
-                                   : ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[i][j] / sc, 0.0f, 0, false) & 0xFFu);
-        }
-        const int tl = rr + 32 * i;
-        if (TRANSPOSE_OUT) {
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                tile[cc * 8 + j][tl] = (uint8_t)code[j];
-        } else {
-            const int64_t tk = tok0 + tl;
-            uint8_t *qr = q + tk * ldq;
-            if (full) {
-                *reinterpret_cast<uint2 *>(qr + c0) =
-                    make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-                               code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
-            } else if (tk < tokens) {
-#pragma unroll
-                for (int j = 0; j < 8; j++)
-                    if (c0 + j < cols)
-                        qr[c0 + j] = (uint8_t)code[j];
-            }
-        }
-    }
+        word[j] = quant4(v[0][j], v[1][j], v[2][j], v[3][j], make_divider(scl[cc * 8 + j]));
     if (TRANSPOSE_OUT) {
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            tile[cc * 8 + j][rq] = word[j];
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < 2; it++) {
@@ -244,12 +239,194 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
             if (c >= cols)
                 continue;
             uint8_t *dst = q + c * ldq + tk;
+            const uint32_t *src = &tile[row][seg * 4];
             if (tk + 16 <= tokens) {
-                *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&tile[row][seg * 16]);
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(src[0], src[1], src[2], src[3]);
             } else {
                 for (int e = 0; e < 16; e++)
                     if (tk + e < tokens)
-                        dst[e] = tile[row][seg * 16 + e];
+                        dst[e] = (uint8_t)((src[e >> 2] >> (8 * (e & 3))) & 0xFF);
+            }
+        }
+    } else {
+        // untransposed: row (token) 4*rq+i gets byte i of each column word
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t tk = tok0 + 4 * rq + i;
+            uint32_t b[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                b[j] = (word[j] >> (8 * i)) & 0xFFu;
+            uint8_t *qr = q + tk * ldq;
+            if (full) {
+                *reinterpret_cast<uint2 *>(qr + c0) =
+                    make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                               b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+            } else if (tk < tokens) {
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    if (c0 + j < cols)
+                        qr[c0 + j] = (uint8_t)b[j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dual quantiser: one read of x [tokens][cols] produces both the 1x128
+// row-blocked copy (each token's 128-column blocks) and the token-blocked
+// copy (each column's 128-token blocks), exactly as the two separate kernels
+// do.  One workgroup per 128-token x 128-column tile, which holds one block
+// of each kind per token and per column.  Thread t owns columns 8*(t%16) .. +7
+// of the 8 consecutive tokens 8*(t/16) .. +7 (64 values in registers).
+// Row amax: cross-lane max over the 16 lanes with equal t/16.  Column amax:
+// per-thread max over its 8 tokens, cross-lane max over lanes with equal
+// t%16, then across the 4 waves through LDS.
+// ---------------------------------------------------------------------------
+template <typename T, bool TRANSPOSE_OUT>
+__global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x, int64_t tokens,
+                                                         int64_t cols, int64_t ldx,
+                                                         uint8_t *__restrict__ qr, int64_t ldqr,
+                                                         float *__restrict__ sr, int64_t nbr,
+                                                         uint8_t *__restrict__ qt, int64_t ldqt,
+                                                         float *__restrict__ st, int64_t ntb)
+{
+    __shared__ float red[4][128];
+    __shared__ float scl[128];
+    __shared__ uint32_t tile[128][32 + 1];   // [column][token/4] codes, odd stride
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int cc = t & 15, rq = t >> 4;
+    const int64_t tok0 = (int64_t)blockIdx.y * 128;
+    const int64_t col0 = (int64_t)blockIdx.x * 128;
+    const int64_t c0 = col0 + cc * 8;
+    const bool full = (tok0 + 128 <= tokens) && (col0 + 128 <= cols);
+
+    float v[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int64_t tk = tok0 + 8 * rq + i;
+        const T *xr = x + tk * ldx;
+        if (full) {
+            Elem<T>::load8(xr + c0, v[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                v[i][j] = (tk < tokens && c0 + j < cols) ? Elem<T>::load(xr + c0 + j) : 0.0f;
+        }
+    }
+
+    // ---- column (token-block) scales
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        float a = fabsf(v[0][j]);
+#pragma unroll
+        for (int i = 1; i < 8; i++)
+            a = fmaxf(a, fabsf(v[i][j]));
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        a = fmaxf(a, __shfl_xor(a, 32, 64));
+        m[j] = a;
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            red[wave][lane * 8 + j] = m[j];
+    }
+    __syncthreads();
+    if (t < 128) {
+        const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+        const float sc = amax / 448.0f;
+        scl[t] = sc;
+        const int64_t c = col0 + t;
+        if (c < cols) {
+            if (TRANSPOSE_OUT)
+                st[c * ntb + blockIdx.y] = sc;
+            else
+                st[(int64_t)blockIdx.y * cols + c] = sc;
+        }
+    }
+
+    // ---- row blocks: quantise and store while the column scales settle
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int64_t tk = tok0 + 8 * rq + i;
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            a = fmaxf(a, fabsf(v[i][j]));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1)
+            a = fmaxf(a, __shfl_xor(a, off, 16));
+        const float sc = a / 448.0f;
+        const Divider dv = make_divider(sc);
+        const uint32_t lo = quant4(v[i][0], v[i][1], v[i][2], v[i][3], dv);
+        const uint32_t hi = quant4(v[i][4], v[i][5], v[i][6], v[i][7], dv);
+        uint8_t *q = qr + tk * ldqr;
+        if (full) {
+            *reinterpret_cast<uint2 *>(q + c0) = make_uint2(lo, hi);
+        } else if (tk < tokens) {
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                if (c0 + j < cols)
+                    q[c0 + j] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFF);
+        }
+        if (cc == 0 && tk < tokens)
+            sr[tk * nbr + blockIdx.x] = sc;
+    }
+    __syncthreads();
+
+    // ---- token blocks
+    uint32_t word[2][8];   // word[h][j]: codes of tokens 8rq+4h .. +3 of column cc*8+j
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const Divider dv = make_divider(scl[cc * 8 + j]);
+        word[0][j] = quant4(v[0][j], v[1][j], v[2][j], v[3][j], dv);
+        word[1][j] = quant4(v[4][j], v[5][j], v[6][j], v[7][j], dv);
+    }
+    if (TRANSPOSE_OUT) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            tile[cc * 8 + j][2 * rq] = word[0][j];
+            tile[cc * 8 + j][2 * rq + 1] = word[1][j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 4; it++) {
+            const int chunk = t + 256 * it;
+            const int row = chunk >> 3, seg = chunk & 7;
+            const int64_t c = col0 + row;
+            const int64_t tk = tok0 + seg * 16;
+            if (c >= cols)
+                continue;
+            uint8_t *dst = qt + c * ldqt + tk;
+            const uint32_t *src = &tile[row][seg * 4];
+            if (tk + 16 <= tokens) {
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(src[0], src[1], src[2], src[3]);
+            } else {
+                for (int e = 0; e < 16; e++)
+                    if (tk + e < tokens)
+                        dst[e] = (uint8_t)((src[e >> 2] >> (8 * (e & 3))) & 0xFF);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int64_t tk = tok0 + 8 * rq + i;
+            uint32_t b[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                b[j] = (word[i >> 2][j] >> (8 * (i & 3))) & 0xFFu;
+            uint8_t *q = qt + tk * ldqt;
+            if (full) {
+                *reinterpret_cast<uint2 *>(q + c0) =
+                    make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                               b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+            } else if (tk < tokens) {
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    if (c0 + j < cols)
+                        q[c0 + j] = (uint8_t)b[j];
             }
         }
     }
@@ -261,10 +438,10 @@ hipError_t launch_quant_act(const void *x, bool bf16, int64_t rows, int64_t cols
                             uint8_t *q, int64_t ldq, float *s, hipStream_t st)
 {
     const int64_t nb = (cols + 127) / 128;
-    const int64_t nblocks = rows * nb;
-    if (nblocks == 0)
+    const int64_t groups = rows * ((nb + BPG - 1) / BPG);
+    if (groups == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((nblocks + 15) / 16));
+    const dim3 grid((unsigned)((groups + 15) / 16));
     if (bf16)
         hipLaunchKernelGGL(quant_act_kernel<uint16_t>, grid, dim3(256), 0, st,
                            (const uint16_t *)x, rows, cols, ldx, q, ldq, s, nb);
@@ -282,10 +459,10 @@ hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t c
         return hipSuccess;
     const dim3 grid((unsigned)cb, (unsigned)rb);
     if (bf16)
-        hipLaunchKernelGGL(quant_weight_kernel<uint16_t>, grid, dim3(256), 0, st,
+        hipLaunchKernelGGL(quant_weight_kernel<uint16_t>, grid, dim3(1024), 0, st,
                            (const uint16_t *)w, rows, cols, ldw, q, ldq, s, cb);
     else
-        hipLaunchKernelGGL(quant_weight_kernel<float>, grid, dim3(256), 0, st, (const float *)w,
+        hipLaunchKernelGGL(quant_weight_kernel<float>, grid, dim3(1024), 0, st, (const float *)w,
                            rows, cols, ldw, q, ldq, s, cb);
     return hipGetLastError();
 }
@@ -313,6 +490,32 @@ hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int6
             hipLaunchKernelGGL((quant_transpose_kernel<float, false>), grid, dim3(256), 0, st,
                                (const float *)x, tokens, cols, ldx, q, ldq, s, ntb);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t cols, int64_t ldx,
+                             uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
+                             int64_t ldqt, float *st, hipStream_t stream)
+{
+    const int64_t ntb = (tokens + 127) / 128, ncb = (cols + 127) / 128;
+    if (ntb == 0 || ncb == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)ncb, (unsigned)ntb);
+#define PURO_DUAL(T, TR)                                                                            \
+    hipLaunchKernelGGL((quant_dual_kernel<T, TR>), grid, dim3(256), 0, stream, (const T *)x, tokens, \
+                       cols, ldx, qr, ldqr, sr, ncb, qt, ldqt, st, ntb)
+    if (bf16) {
+        if (transpose_out)
+            PURO_DUAL(uint16_t, true);
+        else
+            PURO_DUAL(uint16_t, false);
+    } else {
+        if (transpose_out)
+            PURO_DUAL(float, true);
+        else
+            PURO_DUAL(float, false);
+    }
+#undef PURO_DUAL
     return hipGetLastError();
 }
 

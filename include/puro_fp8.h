@@ -33,6 +33,8 @@
  *   - On success the work is enqueued on `stream` (NULL = the null stream) and
  *     the call returns without synchronising.  Results are defined once the
  *     stream reaches that point.
+ *   - Every extent and leading dimension is at most 2^23 (8,388,608), else
+ *     PURO_ERR_SHAPE.
  *   - The library allocates nothing and keeps no per-call state; calls are
  *     reentrant.  No C++ exception crosses this interface.
  *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
@@ -110,6 +112,22 @@ puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t row
 puro_status_t puro_fp8_quant_transpose(const void *x, puro_dtype_t xdt, int64_t tokens,
                                        int64_t cols, int64_t ldx, int transpose_out, uint8_t *q,
                                        int64_t ldq, float *s, hipStream_t stream);
+
+/*
+ * Dual quantiser: one read of x [tokens][cols] (FP32 or BF16, stride ldx)
+ * produces both copies a linear layer needs of its input X (or of its output
+ * gradient dY), with exactly the codes and scales of the two separate calls:
+ *   q_row [tokens][cols] (stride ldq_row), s_row [tokens][ceil(cols/128)]
+ *        -- as puro_fp8_quant_act (1x128 blocks along each row);
+ *   q_tok, s_tok -- as puro_fp8_quant_transpose with the same transpose_out
+ *        (128-token blocks of each column).
+ * Reading the BF16 input once instead of twice is the saving.  The two output
+ * pairs must not overlap each other or x.
+ */
+puro_status_t puro_fp8_quant_dual(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                  int64_t ldx, uint8_t *q_row, int64_t ldq_row, float *s_row,
+                                  int transpose_out, uint8_t *q_tok, int64_t ldq_tok, float *s_tok,
+                                  hipStream_t stream);
 
 /*
  * Workspace bytes puro_fp8_gemm needs for this problem (0 = none).  Returns 0

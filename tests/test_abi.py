@@ -98,6 +98,24 @@ def test_quant_transpose_validation():
     assert _qt(x=NUL, q=NUL, s=NUL, tokens=0, ldq=0) == OK
 
 
+def _qd(x=P, dt=1, tokens=256, cols=128, ldx=128, qr=P, ldqr=128, sr=P, t=1, qt=P, ldqt=256, st=P):
+    return pf.lib().puro_fp8_quant_dual(x, dt, tokens, cols, ldx, qr, ldqr, sr, t, qt, ldqt, st, None)
+
+
+def test_quant_dual_validation():
+    assert _qd(t=3) == ENUM
+    assert _qd(dt=9) == ENUM
+    assert _qd(ldqr=64) == SHAPE          # row copy rows hold `cols` codes
+    assert _qd(ldqt=128) == SHAPE         # transposed copy rows hold `tokens` codes
+    assert _qd(t=0, ldqt=64) == SHAPE     # untransposed copy rows hold `cols` codes
+    assert _qd(tokens=-2) == SHAPE
+    assert _qd(qr=NUL) == NULL
+    assert _qd(st=NUL) == NULL
+    assert _qd(ldqr=136) == ALIGN
+    assert _qd(qt=P_ODD) == ALIGN
+    assert _qd(x=NUL, qr=NUL, sr=NUL, qt=NUL, st=NUL, tokens=0, ldqt=0) == OK
+
+
 def _gemm(layout=0, M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, bg=1, C=P,
           cdt=1, ldc=256, ws=NUL, wsb=0):
     return pf.lib().puro_fp8_gemm(layout, M, N, K, A, lda, sA, B, ldb, sB, bg, C, cdt, ldc, ws,

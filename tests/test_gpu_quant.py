@@ -59,6 +59,9 @@ def _adversarial(rows, cols, seed):
             x[r, seg] = (rng.standard_normal(128) * 1e-9).astype(np.float32)
             x[r, b * 128] = 1.0
             x[r, b * 128 + 1] = -0.0
+        else:             # scales either side of 2^-80 (where the kernels stop using the reciprocal)
+            x[r, seg] *= np.float32(2.0) ** rng.integers(-76, -62)
+            x[r, seg][rng.integers(0, 128, 8)] *= np.float32(2.0 ** -20)
     return x
 
 
@@ -142,3 +145,28 @@ def test_padding_is_untouched(dev):
     pf.puro_fp8_quant_act(to_dev(x, ld=208), q=q)
     torch.cuda.synchronize()
     assert (buf[:, 200:] == 0x5A).all()
+
+
+DUAL_CASES = [
+    ("layer_x_bf16", lambda: synth.normal((1024, 2048), 1.0, synth.seed_of(3, 0, 1), "bf16"), None),
+    ("dy_bf16", lambda: synth.normal((512, 6144), 1e-3, synth.seed_of(3, 0, 10), "bf16"), None),
+    ("outlier_bf16", lambda: synth.outlier_activations(512, 768, 195)[0], None),
+    ("lognormal_bf16", lambda: synth.lognormal_gradients(384, 256, 196, random_sign=True), None),
+    ("adversarial_f32", lambda: _adversarial(256, 512, 197), None),
+    ("adversarial_bf16", lambda: synth.f32_to_bf16_bits(_adversarial(256, 1024, 198)), None),
+    ("ragged_bf16", lambda: synth.normal((300, 200), 1.0, 199, "bf16"), 208),
+    ("ragged_f32", lambda: synth.normal((129, 65), 1.0, 200), 80),
+]
+
+
+@pytest.mark.parametrize("transpose_out", [True, False])
+@pytest.mark.parametrize("name,make,ld", DUAL_CASES, ids=[c[0] for c in DUAL_CASES])
+def test_quant_dual_bit_exact(dev, name, make, ld, transpose_out):
+    """One read, two outputs: equal to the oracle's row quantiser and token quantiser."""
+    x = make()
+    qr_ref, sr_ref = oracle.quant_act(x)
+    qt_ref, st_ref = oracle.quant_transpose(x, transpose_out=transpose_out)
+    qr, sr, qt, st = pf.puro_fp8_quant_dual(to_dev(x, ld=ld), transpose_out)
+    torch.cuda.synchronize()
+    _assert_same(qr, sr, qr_ref, sr_ref, name + " rows")
+    _assert_same(qt, st, qt_ref, st_ref, name + " tokens")
