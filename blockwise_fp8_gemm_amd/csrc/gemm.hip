@@ -364,16 +364,18 @@ struct FastCfg {
     static constexpr int LOADS = TM / 8 / NW + TN / 8 / NW + 1;
 };
 
-// 256 x 256 workgroup tiles (8 waves of 128 x 64, two LDS stages) and
-// 256 x 128 tiles (8 waves of 64 x 64, three LDS stages).
+// 256 x 256 workgroup tiles (8 waves of 128 x 64, two LDS stages, one
+// workgroup per CU) and 128 x 128 tiles (4 waves of 64 x 64, two LDS stages,
+// two workgroups per CU).
 typedef FastCfg<2, 4, 8, 4, 2> CfgL;
-typedef FastCfg<4, 2, 4, 4, 3> CfgS;
+typedef FastCfg<2, 2, 4, 4, 2> CfgQ;
+enum { CFG_L = 0, CFG_Q = 1 };
 
 // Split-K: workgroup b handles K blocks [kb_lo, kb_hi) of split s = b / tiles
 // and, with OUT_PARTIAL, stores FP32 partial sums to ws[s][M][N] (row stride N)
 // instead of C; gemm_split_reduce then adds the splits in order.
 template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL>
-__global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n,
+__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n,
                                                                  int splits, float *ws)
 {
     constexpr bool A_KMAJ = (LAYOUT != 2);
@@ -481,10 +483,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int
         const uint8_t *tb = lds[buf] + A_BYTES;
         const int wrow = wm * IT * 16, wcol = wn * JT * 16;
 
+        // B's scales: with 128x128 weight tiles the wave's JT * 16 columns lie in
+        // one tile, so one scale serves them all and sA * sB is formed once per
+        // row; with 1x128 blocks each lane's column has its own scale.
+        static_assert(!BGRAN || 128 % (JT * 16) == 0, "wave columns within one weight tile");
         float sbv[JT];
 #pragma unroll
         for (int j = 0; j < JT; j++)
-            sbv[j] = BGRAN ? lds_sc[buf][TM + ((wcol + j * 16) >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)];
+            sbv[j] = BGRAN ? lds_sc[buf][TM + (wcol >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)];
 
         V8H4 bh[JT];
 #pragma unroll
@@ -505,6 +511,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int
         for (int i = 0; i < IT; i++) {
             const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sc[buf][wrow + i * 16 + 4 * (lane >> 4)]);
             const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+            float sab[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                sab[r] = sa[r] * sbv[0];
+            auto scale = [&](int j, int r) { return BGRAN ? sab[r] : sa[r] * sbv[j]; };
             if (INTERLEAVE) {
                 v4f P[JT];
 #pragma unroll
@@ -523,7 +534,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int
                 for (int j = 0; j < JT; j++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        acc[i][j][r] = fmaf(sa[r] * sbv[j], P[j][r], acc[i][j][r]);
+                        acc[i][j][r] = fmaf(scale(j, r), P[j][r], acc[i][j][r]);
             } else {
                 if (i > 0)
                     araw = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
@@ -537,30 +548,62 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_fast_kernel(GemmArgs p, int
                         P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[q], bh[j].c[q], P, 0, 0, 0);
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        acc[i][j][r] = fmaf(sa[r] * sbv[j], P[r], acc[i][j][r]);
+                        acc[i][j][r] = fmaf(scale(j, r), P[r], acc[i][j][r]);
                 }
             }
         }
         buf = (buf + 1 == STAGES) ? 0 : buf + 1;
     }
 
+    // Epilogue.  Each wave passes its results through a private LDS strip of
+    // 16 rows x JT*16 columns so that every lane stores 16 contiguous bytes of
+    // one row (the MFMA layout gives a lane one column of four rows).  The
+    // strips live in stage `buf`, which no wave reads any more: every wave has
+    // passed the last K block's barrier, after which only the last block's
+    // stage can still be in use, and no copy into `buf` is in flight.
+    constexpr int CW = JT * 16;                              // strip width
+    constexpr int SST = CW + 4;                              // row stride (floats): 4 row groups hit disjoint banks
+    constexpr int CH = (CBF16 && !OUT_PARTIAL) ? 8 : 4;      // elements per 16-byte store
+    constexpr int NCH = 16 * CW / CH;                        // 16-byte chunks per strip
+    static_assert(NCH % 64 == 0, "whole chunks per lane");
+    static_assert(16 * SST * 4 * NW <= A_BYTES + B_BYTES, "strips fit in one stage");
+    float *strip = reinterpret_cast<float *>(lds[buf]) + wave * 16 * SST;
     const int wrow = wm * IT * 16, wcol = wn * JT * 16;
 #pragma unroll
-    for (int i = 0; i < IT; i++)
+    for (int i = 0; i < IT; i++) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int64_t m = m0 + wrow + i * 16 + 4 * (lane >> 4) + r;
+        for (int j = 0; j < JT; j++)
 #pragma unroll
-            for (int j = 0; j < JT; j++) {
-                const int64_t n = n0 + wcol + j * 16 + (lane & 15);
-                if (OUT_PARTIAL)
-                    ws[((int64_t)split * p.M + m) * p.N + n] = acc[i][j][r];
-                else if (CBF16)
-                    reinterpret_cast<uint16_t *>(p.C)[m * p.ldc + n] = to_bf16(acc[i][j][r]);
-                else
-                    reinterpret_cast<float *>(p.C)[m * p.ldc + n] = acc[i][j][r];
+            for (int r = 0; r < 4; r++)
+                strip[(4 * (lane >> 4) + r) * SST + j * 16 + (lane & 15)] = acc[i][j][r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int t = 0; t < NCH / 64; t++) {
+            const int c = t * 64 + lane;
+            const int row = c / (CW / CH), col = (c % (CW / CH)) * CH;
+            const float *src = strip + row * SST + col;
+            const float4 v0 = *reinterpret_cast<const float4 *>(src);
+            const int64_t m = m0 + wrow + i * 16 + row, n = n0 + wcol + col;
+            if (OUT_PARTIAL) {
+                *reinterpret_cast<float4 *>(ws + ((int64_t)split * p.M + m) * p.N + n) = v0;
+            } else if (CBF16) {
+                const float4 v1 = *reinterpret_cast<const float4 *>(src + 4);
+                uint4 o;
+                o.x = (uint32_t)to_bf16(v0.x) | ((uint32_t)to_bf16(v0.y) << 16);
+                o.y = (uint32_t)to_bf16(v0.z) | ((uint32_t)to_bf16(v0.w) << 16);
+                o.z = (uint32_t)to_bf16(v1.x) | ((uint32_t)to_bf16(v1.y) << 16);
+                o.w = (uint32_t)to_bf16(v1.z) | ((uint32_t)to_bf16(v1.w) << 16);
+                *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.C) + m * p.ldc + n) = o;
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.C) + m * p.ldc + n) = v0;
             }
         }
+    }
 }
 
 // C[m][n] = sum over s = 0 .. splits-1, in that order, of ws[s][m][n]; four
@@ -594,36 +637,43 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(const float *__restrict
 // Launch plan for an aligned problem: tile configuration and number of K splits.
 struct FastPlan {
     bool ok;       // aligned fast path applies
-    bool large;    // CfgL (256 x 256) rather than CfgS (256 x 128)
+    int cfg;       // CFG_L or CFG_Q
     int splits;    // K splits (1 = none)
 };
 
 constexpr int kComputeUnits = 256;
 
+// Picks the candidate with the least estimated time.  The estimate uses
+// per-K-block step times measured on gfx950 with every CU busy: a 256 x 256
+// tile (one workgroup per CU) takes about 4.4 us per K block; a 128 x 128 tile
+// about 2.3 us when two share a CU and 1.8 us alone.  Workgroups are spread
+// evenly over the CUs, so the busiest CU sets the time.  Splitting K adds
+// the partial sums, (splits + 1) M N 4 bytes moved at about 4 TB/s, and the
+// reduction launch.
 FastPlan fast_plan(int64_t M, int64_t N, int64_t K)
 {
-    FastPlan best = {false, false, 1};
-    if (K <= 0 || K % 128 || M % CfgS::TM || N % CfgS::TN)
+    FastPlan best = {false, CFG_Q, 1};
+    if (K <= 0 || K % 128 || M % CfgQ::TM || N % CfgQ::TN)
         return best;
     const int64_t KB = K / 128;
-    double best_cost = 1e300;
-    for (int large = 0; large < 2; large++) {
-        const int TM = large ? CfgL::TM : CfgS::TM, TN = large ? CfgL::TN : CfgS::TN;
+    double best_us = 1e300;
+    for (int cfg : {CFG_L, CFG_Q}) {
+        const int TM = cfg == CFG_L ? CfgL::TM : CfgQ::TM, TN = cfg == CFG_L ? CfgL::TN : CfgQ::TN;
         if (M % TM || N % TN)
             continue;
         const int64_t tiles = (M / TM) * (N / TN);
         for (int sp = 1; sp <= 8; sp *= 2) {
             if (sp > 1 && KB / sp < 4)
                 break;
-            const int64_t rounds = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
-            // time in units of one 256 x 128 x 128 block step (about 2 us): rounds x steps x tile area
-            double cost = (double)rounds * (double)((KB + sp - 1) / sp) * (large ? 2.0 : 1.0) *
-                          (large ? 0.9 : 1.0);
-            if (sp > 1)   // partial sums written and re-read: (sp + 1) M N 4 bytes at ~4 TB/s
-                cost += (double)(sp + 1) * M * N * 4.0 / 4e12 / 2e-6;
-            if (cost < best_cost) {
-                best_cost = cost;
-                best = {true, large != 0, sp};
+            const double steps = (double)((KB + sp - 1) / sp);
+            const int64_t per_cu = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
+            double us = cfg == CFG_L ? (double)per_cu * steps * 4.4 + 5.0
+                                     : (double)(per_cu / 2) * steps * 2.3 + (double)(per_cu % 2) * steps * 1.8;
+            if (sp > 1)
+                us += (double)(sp + 1) * (double)M * (double)N * 4.0 / 4e6 + 5.0;
+            if (us < best_us) {
+                best_us = us;
+                best = {true, cfg, sp};
             }
         }
     }
@@ -654,9 +704,9 @@ hipError_t launch_fast_cfg(const GemmArgs &a, int splits, float *ws, hipStream_t
 template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_fast(const GemmArgs &a, const FastPlan &plan, float *ws, hipStream_t st)
 {
-    if (plan.large)
+    if (plan.cfg == CFG_L)
         return launch_fast_cfg<CfgL, LAYOUT, BGRAN, CBF16>(a, plan.splits, ws, st);
-    return launch_fast_cfg<CfgS, LAYOUT, BGRAN, CBF16>(a, plan.splits, ws, st);
+    return launch_fast_cfg<CfgQ, LAYOUT, BGRAN, CBF16>(a, plan.splits, ws, st);
 }
 
 template <int LAYOUT, int BGRAN, bool CBF16>
