@@ -6,7 +6,9 @@ layers of all 28 Transformer layers: the seven unfused projections
 (dX = dY W) and weight gradient (dW = dY^T X), with every quantiser inside
 the timed region: weights in 128x128 tiles, and each layer input X and each
 output gradient dY quantised both ways in one read (1x128 along features for
-the forward / data-gradient GEMM, 128-token blocks for the weight gradient).  Shapes come from the
+the forward / data-gradient GEMM, 128-token blocks for the weight gradient).
+Products that a training step can run together share grouped launches
+(q/k/v, gate/up, and a layer's seven weight gradients).  Shapes come from the
 Puro-2B-Base model card (Qwen3-1.7B configuration: hidden 2,048, FFN 6,144,
 16 / 8 heads, 28 layers; sequence length 4,096, micro-batch 2).
 
@@ -66,17 +68,15 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     def nb(n):
         return (n + 127) // 128
 
-    # Reused per-layer work buffers, sized for the largest use.
-    max_in = max(k for _, _, k, _ in synth.LAYER_GEMMS)
-    max_out = max(n for _, n, _, _ in synth.LAYER_GEMMS)
+    # Per-layer work buffers, reused by every layer.
     qx = {name: torch.empty((tokens, c), dtype=u8, device=dev) for name, c in synth.LAYER_INPUTS}
     sx = {name: torch.empty((tokens, nb(c)), dtype=f32, device=dev) for name, c in synth.LAYER_INPUTS}
     qxt = {name: torch.empty((c, tokens), dtype=u8, device=dev) for name, c in synth.LAYER_INPUTS}
     sxt = {name: torch.empty((c, nb(tokens)), dtype=f32, device=dev) for name, c in synth.LAYER_INPUTS}
-    qdy = torch.empty((tokens, max_out), dtype=u8, device=dev)
-    sdy = torch.empty((tokens, nb(max_out)), dtype=f32, device=dev)
-    qdyt = torch.empty((max_out, tokens), dtype=u8, device=dev)
-    sdyt = torch.empty((max_out, nb(tokens)), dtype=f32, device=dev)
+    qdy = {g: torch.empty((tokens, n), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    sdy = {g: torch.empty((tokens, nb(n)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    qdyt = {g: torch.empty((n, tokens), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    sdyt = {g: torch.empty((n, nb(tokens)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     qw = {g: torch.empty((n, k), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     sw = {g: torch.empty((nb(n), nb(k)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     y = {g: torch.empty((tokens, n), dtype=bf16, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
@@ -84,20 +84,38 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     dw = {g: torch.empty((n, k), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, y, dx, dw]
 
-    # one workspace for every call that splits K (calls run in stream order)
-    ws_bytes = 0
-    for g, n, k, _ in synth.LAYER_GEMMS:
-        ws_bytes = max(ws_bytes, pf.puro_fp8_gemm_workspace_size("NT", tokens, n, k, "128x128"),
-                       pf.puro_fp8_gemm_workspace_size("NN", tokens, k, n, "128x128"),
-                       pf.puro_fp8_gemm_workspace_size("NT", n, k, tokens, "1x128"))
-    ws = torch.empty(max(ws_bytes, 256), dtype=u8, device=dev)
-    keep.append(ws)
-    WS, WSB = P(ws), ctypes.c_size_t(ws_bytes)
-
     BF16, F32 = pf.PURO_BF16, pf.PURO_F32
     NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
     S1, S128 = pf.BGRAN["1x128"], pf.BGRAN["128x128"]
     T = tokens
+    shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
+
+    def grouped(layout, bgran, cdt, descs, name, flops):
+        arr = (pf.GemmDesc * len(descs))(*descs)
+        keep.append(arr)
+        plan.add(L.puro_fp8_gemm_grouped, (layout, bgran, cdt, arr, len(descs), stream_ptr), "gemm", name, flops)
+
+    def fwd(g):
+        n, k, src = shape[g]
+        return pf.GemmDesc(T, n, k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]), P(y[g]), n)
+
+    def dgrad(g):
+        n, k, src = shape[g]
+        return pf.GemmDesc(T, k, n, P(qdy[g]), n, P(sdy[g]), P(qw[g]), k, P(sw[g]), P(dx[g]), k)
+
+    def wgrad(g):
+        n, k, src = shape[g]
+        return pf.GemmDesc(n, k, T, P(qdyt[g]), T, P(sdyt[g]), P(qxt[src]), T, P(sxt[src]), P(dw[g]), k)
+
+    def fl(gs):
+        return sum(2.0 * T * shape[g][0] * shape[g][1] for g in gs)
+
+    # Products that can run together share one grouped launch, in the order a
+    # training step allows: the q, k and v projections of one input, the gate
+    # and up projections of one input; backward from the last projection to
+    # the first; the weight gradients of a layer once its output gradients exist.
+    FWD_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    DGRAD_GROUPS = (("down",), ("gate", "up"), ("o",), ("q", "k", "v"))
     for layer in range(layers):
         xs = {name: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
               for i, (name, c) in enumerate(synth.LAYER_INPUTS)}
@@ -106,31 +124,29 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
         dys = {g: synth.device_normal((T, n), 1e-3, synth.seed_of(4, layer, 20 + j), "bf16", dev)
                for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
         keep += [xs, wts, dys]
-        # forward: each distinct input quantised once, both ways (the token-blocked
-        # copy is kept for the weight gradient); each weight once; Y = X W^T
+        # forward: each weight quantised once (128x128 tiles), each distinct input
+        # once both ways (the 128-token copy is kept for the weight gradient)
+        for g, n, k, src in synth.LAYER_GEMMS:
+            plan.add(L.puro_fp8_quant_weight, (P(wts[g]), F32, n, k, k, P(qw[g]), k, P(sw[g]), stream_ptr),
+                     "quant_weight", "quant_weight", 0, n * k * (4 + 1) + nb(n) * nb(k) * 4)
         for name, c in synth.LAYER_INPUTS:
             plan.add(L.puro_fp8_quant_dual, (P(xs[name]), BF16, T, c, c, P(qx[name]), c, P(sx[name]), 1,
                                              P(qxt[name]), T, P(sxt[name]), stream_ptr),
                      "quant_dual", "quant_dual", 0, T * c * (2 + 2 + 8 / 128))
-        for g, n, k, src in synth.LAYER_GEMMS:
-            plan.add(L.puro_fp8_quant_weight, (P(wts[g]), F32, n, k, k, P(qw[g]), k, P(sw[g]), stream_ptr),
-                     "quant_weight", "quant_weight", 0, n * k * (4 + 1) + nb(n) * nb(k) * 4)
-            plan.add(L.puro_fp8_gemm, (NT, T, n, k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]),
-                                       S128, P(y[g]), BF16, n, WS, WSB, stream_ptr),
-                     "gemm", "gemm_fwd_NT_128x128_bf16", 2.0 * T * n * k)
-        # backward, per projection: dY quantised both ways in one read, then the
-        # data gradient dX = dY W (the forward's quantised W) and the weight
-        # gradient dW = dY^T X (token-blocked copies)
-        for g, n, k, src in synth.LAYER_GEMMS:
-            plan.add(L.puro_fp8_quant_dual, (P(dys[g]), BF16, T, n, n, P(qdy), n, P(sdy), 1, P(qdyt), T,
-                                             P(sdyt), stream_ptr),
+        for gs in FWD_GROUPS:
+            grouped(NT, S128, BF16, [fwd(g) for g in gs], "gemm_fwd_NT_128x128_bf16", fl(gs))
+        # backward: each output gradient quantised both ways in one read; data
+        # gradients dX = dY W with the forward's quantised W; weight gradients
+        # dW = dY^T X on the 128-token copies
+        for g in ("down", "gate", "up", "o", "q", "k", "v"):
+            n = shape[g][0]
+            plan.add(L.puro_fp8_quant_dual, (P(dys[g]), BF16, T, n, n, P(qdy[g]), n, P(sdy[g]), 1, P(qdyt[g]), T,
+                                             P(sdyt[g]), stream_ptr),
                      "quant_dual", "quant_dual", 0, T * n * (2 + 2 + 8 / 128))
-            plan.add(L.puro_fp8_gemm, (NN, T, k, n, P(qdy), n, P(sdy), P(qw[g]), k, P(sw[g]), S128,
-                                       P(dx[g]), BF16, k, WS, WSB, stream_ptr),
-                     "gemm", "gemm_dgrad_NN_128x128_bf16", 2.0 * T * n * k)
-            plan.add(L.puro_fp8_gemm, (NT, n, k, T, P(qdyt), T, P(sdyt), P(qxt[src]), T, P(sxt[src]),
-                                       S1, P(dw[g]), F32, k, WS, WSB, stream_ptr),
-                     "gemm", "gemm_wgrad_NT_1x128_f32", 2.0 * T * n * k)
+        for gs in DGRAD_GROUPS:
+            grouped(NN, S128, BF16, [dgrad(g) for g in gs], "gemm_dgrad_NN_128x128_bf16", fl(gs))
+        gs = [g for g, _, _, _ in synth.LAYER_GEMMS]
+        grouped(NT, S1, F32, [wgrad(g) for g in gs], "gemm_wgrad_NT_1x128_f32", fl(gs))
     return plan, keep
 
 

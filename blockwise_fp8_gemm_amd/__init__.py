@@ -38,6 +38,14 @@ class PuroError(RuntimeError):
         super().__init__("%s failed: %s (status %d)" % (what, puro_status_string(status), status))
 
 
+class GemmDesc(ctypes.Structure):
+    """puro_gemm_desc_t: one problem of puro_fp8_gemm_grouped."""
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("sA", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("sB", ctypes.c_void_p),
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
+
+
 def lib():
     """Load libpuro_fp8.so; raises if it has not been built."""
     global _lib
@@ -60,6 +68,8 @@ def lib():
         L.puro_fp8_gemm.restype = i32
         L.puro_fp8_gemm.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32,
                                     i64, vp, ctypes.c_size_t, vp]
+        L.puro_fp8_gemm_grouped.restype = i32
+        L.puro_fp8_gemm_grouped.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, vp]
         L.puro_status_string.restype = ctypes.c_char_p
         L.puro_status_string.argtypes = [i32]
         L.puro_fp8_version.restype = i32
@@ -266,3 +276,39 @@ def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat1
                                PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32, _ld(C),
                                _ptr(workspace), ws_bytes, _stream(stream)), "puro_fp8_gemm")
     return C
+
+
+def gemm_descs(layout, problems, bgran="128x128", out_dtype=torch.bfloat16):
+    """Checked descriptors for puro_fp8_gemm_grouped.  problems: a list of
+    (A, sA, B, sB) or (A, sA, B, sB, C); missing outputs are allocated.
+    Returns (ctypes array of GemmDesc, list of C)."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype is float32 or bfloat16")
+    descs = (GemmDesc * max(len(problems), 1))()
+    outs = []
+    for i, prob in enumerate(problems):
+        A, sA, B, sB = prob[:4]
+        C = prob[4] if len(prob) > 4 else None
+        M, N, K = gemm_dims(layout, A, B)
+        if A.dtype != torch.uint8 or B.dtype != torch.uint8:
+            raise TypeError("A and B hold E4M3 codes (torch.uint8)")
+        sa_shape, sb_shape = scale_shapes(layout, bgran, M, N, K)
+        _need_dense(sA, sa_shape, "sA")
+        _need_dense(sB, sb_shape, "sB")
+        if C is None:
+            C = empty_2d(M, N, out_dtype, A.device)
+        _need(C, (M, N), out_dtype, "C")
+        descs[i] = GemmDesc(M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C), _ld(C))
+        outs.append(C)
+    return descs, outs
+
+
+def puro_fp8_gemm_grouped(layout, problems, bgran="128x128", out_dtype=torch.bfloat16, stream=None):
+    """Independent blockwise-scaled E4M3 GEMMs sharing layout, B-scale
+    granularity and output dtype, in as few launches as possible.
+    problems: list of (A, sA, B, sB) or (A, sA, B, sB, C); returns the list of C."""
+    descs, outs = gemm_descs(layout, problems, bgran, out_dtype)
+    _check(lib().puro_fp8_gemm_grouped(LAYOUTS[layout], BGRAN[bgran],
+                                       PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32,
+                                       descs, len(problems), _stream(stream)), "puro_fp8_gemm_grouped")
+    return outs

@@ -3,6 +3,8 @@
 #include "../../include/puro_fp8.h"
 #include "kernels.h"
 
+#include <vector>
+
 namespace {
 
 // Largest extent accepted along any dimension (keeps every grid dimension and
@@ -214,6 +216,39 @@ puro_status_t puro_fp8_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t 
         if (M == 0 || N == 0)
             return PURO_OK;
         return from_hip(puro::launch_gemm(p, workspace, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                    const puro_gemm_desc_t *problems, int count, hipStream_t stream)
+{
+    try {
+        if (count < 0 || count > 4096)
+            return PURO_ERR_SHAPE;
+        if (count > 0 && !problems)
+            return PURO_ERR_NULL;
+        std::vector<puro::GemmProblem> ps;
+        ps.reserve((size_t)count);
+        for (int i = 0; i < count; i++) {
+            const puro_gemm_desc_t &d = problems[i];
+            const puro_status_t st = check_gemm(layout, d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB,
+                                                bgran, d.C, cdt, d.ldc);
+            if (st != PURO_OK)
+                return st;
+            ps.push_back(make_problem(layout, d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, bgran, d.C,
+                                      cdt, d.ldc));
+        }
+        if (layout != PURO_NT && layout != PURO_NN && layout != PURO_TN)
+            return PURO_ERR_ENUM;
+        if (bgran != PURO_SCALE_1x128 && bgran != PURO_SCALE_128x128)
+            return PURO_ERR_ENUM;
+        if (cdt != PURO_F32 && cdt != PURO_BF16)
+            return PURO_ERR_ENUM;
+        if (ps.empty())
+            return PURO_OK;
+        return from_hip(puro::launch_gemm_group(ps.data(), (int)ps.size(), stream));
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }

@@ -36,6 +36,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
 namespace puro {
 
 namespace {
@@ -374,9 +378,33 @@ enum { CFG_L = 0, CFG_Q = 1 };
 // Split-K: workgroup b handles K blocks [kb_lo, kb_hi) of split s = b / tiles
 // and, with OUT_PARTIAL, stores FP32 partial sums to ws[s][M][N] (row stride N)
 // instead of C; gemm_split_reduce then adds the splits in order.
+// Position of tile t (of tiles_m x tiles_n) in the walk order: groups of 8 tile
+// rows, column by column inside a group, so that the workgroups resident
+// together share A and B panels in L2.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    constexpr int GROUP = 8;
+    const int group = t / (GROUP * tiles_n);
+    const int first_m = group * GROUP;
+    const int gm = min(tiles_m - first_m, GROUP);
+    tm = first_m + (t % (GROUP * tiles_n)) % gm;
+    tn = (t % (GROUP * tiles_n)) / gm;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Maps dispatch index
+// b of a range of n workgroups (n a multiple of 8) so that each XCD gets a
+// contiguous eighth of the range.
+__device__ __forceinline__ int xcd_contiguous(int b, int n)
+{
+    return (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3);
+}
+
+// One workgroup's output tile: rows [m0, m0 + TM) x columns [n0, n0 + TN) of
+// problem p, over K blocks [kb_lo, kb_hi).  With OUT_PARTIAL the FP32 result
+// goes to ws[split][M][N] (row stride N) instead of C.
 template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL>
-__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n,
-                                                                 int splits, float *ws)
+__device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t n0, int64_t kb_lo,
+                                          int64_t kb_hi, int split, float *ws)
 {
     constexpr bool A_KMAJ = (LAYOUT != 2);
     constexpr bool B_KMAJ = (LAYOUT == 0);
@@ -392,25 +420,6 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
-    // Tile order: workgroups are dispatched round-robin over the 8 XCDs; give
-    // each XCD a contiguous run of tiles, walked in groups of 8 tile rows so
-    // that workgroups resident together share A and B panels in that XCD's L2.
-    const int tiles = tiles_m * tiles_n;
-    const int nwg = tiles * splits;
-    int b = blockIdx.x;
-    if ((nwg & 7) == 0)
-        b = (b & 7) * (nwg >> 3) + (b >> 3);
-    const int split = b / tiles;
-    int t = b - split * tiles;
-    const int64_t kb_lo = p.KB * split / splits, kb_hi = p.KB * (split + 1) / splits;
-    constexpr int GROUP = 8;
-    const int group = t / (GROUP * tiles_n);
-    const int first_m = group * GROUP;
-    const int gm = min(tiles_m - first_m, GROUP);
-    const int tm = first_m + (t % (GROUP * tiles_n)) % gm;
-    const int tn = (t % (GROUP * tiles_n)) / gm;
-    const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
-
     float acc[IT][JT][4];
 #pragma unroll
     for (int i = 0; i < IT; i++)
@@ -420,40 +429,51 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, 
             for (int r = 0; r < 4; r++)
                 acc[i][j][r] = 0.0f;
 
+    // The problem's operands, read once.  Scales: thread q copies, for every K
+    // block kb, the scale at sc_base + kb * sc_step: A's scale of tile row q
+    // (q < TM), then B's scales (one per tile column, or one per 128-wide
+    // weight tile), then harmless duplicates of A's first, so that every wave
+    // issues the same copies.
+    const uint8_t *const gA = p.A, *const gB = p.B;
+    const int64_t lda = p.lda, ldb = p.ldb;
+    const float *sc_base;
+    int64_t sc_step;
+    {
+        const int nsb = BGRAN ? TN / 128 : TN;
+        if (tid < TM) {
+            const int64_t m = m0 + tid;
+            sc_base = A_KMAJ ? p.sA + m * p.KB : p.sA + m;
+            sc_step = A_KMAJ ? 1 : p.M;
+        } else if (tid < TM + nsb) {
+            const int64_t q = tid - TM;
+            if (BGRAN) {
+                const int64_t nb = (n0 >> 7) + q;
+                sc_base = B_KMAJ ? p.sB + nb * p.KB : p.sB + nb;
+                sc_step = B_KMAJ ? 1 : p.NB;
+            } else {
+                const int64_t n = n0 + q;
+                sc_base = B_KMAJ ? p.sB + n * p.KB : p.sB + n;
+                sc_step = B_KMAJ ? 1 : p.N;
+            }
+        } else {
+            sc_base = A_KMAJ ? p.sA + m0 * p.KB : p.sA + m0;
+            sc_step = A_KMAJ ? 1 : p.M;
+        }
+    }
+
     auto stage = [&](int64_t kb, int buf) {
         const int64_t k0 = kb * 128;
         uint8_t *ta = lds[buf];
         uint8_t *tb = lds[buf] + A_BYTES;
         if (A_KMAJ)
-            fast_stage_k<TM, NW>(ta, p.A, p.lda, m0, k0, wave, lane);
+            fast_stage_k<TM, NW>(ta, gA, lda, m0, k0, wave, lane);
         else
-            fast_stage_mn<TM, NW>(ta, p.A, p.lda, k0, m0, wave, lane);
+            fast_stage_mn<TM, NW>(ta, gA, lda, k0, m0, wave, lane);
         if (B_KMAJ)
-            fast_stage_k<TN, NW>(tb, p.B, p.ldb, n0, k0, wave, lane);
+            fast_stage_k<TN, NW>(tb, gB, ldb, n0, k0, wave, lane);
         else
-            fast_stage_mn<TN, NW>(tb, p.B, p.ldb, k0, n0, wave, lane);
-        // Scales: lane q of the workgroup copies A's scale of row q (q < TM),
-        // then B's scales (one per column, or one per 128-wide weight tile),
-        // and a harmless duplicate of A's first scale beyond that, so that
-        // every wave issues the same copies.
-        const int nsb = BGRAN ? TN / 128 : TN;
-        const float *src;
-        if (tid < TM) {
-            const int64_t m = m0 + tid;
-            src = A_KMAJ ? p.sA + m * p.KB + kb : p.sA + kb * p.M + m;
-        } else if (tid < TM + nsb) {
-            const int64_t q = tid - TM;
-            if (BGRAN) {
-                const int64_t nb = (n0 >> 7) + q;
-                src = B_KMAJ ? p.sB + nb * p.KB + kb : p.sB + kb * p.NB + nb;
-            } else {
-                const int64_t n = n0 + q;
-                src = B_KMAJ ? p.sB + n * p.KB + kb : p.sB + kb * p.N + n;
-            }
-        } else {
-            src = A_KMAJ ? p.sA + m0 * p.KB + kb : p.sA + kb * p.M + m0;
-        }
-        load_lds4(src, &lds_sc[buf][wave * 64]);
+            fast_stage_mn<TN, NW>(tb, gB, ldb, k0, n0, wave, lane);
+        load_lds4(sc_base + kb * sc_step, &lds_sc[buf][wave * 64]);
     };
 
     // vmcnt(n) immediate for gfx9-family s_waitcnt (expcnt and lgkmcnt left unconstrained)
@@ -569,6 +589,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, 
     static_assert(16 * SST * 4 * NW <= A_BYTES + B_BYTES, "strips fit in one stage");
     float *strip = reinterpret_cast<float *>(lds[buf]) + wave * 16 * SST;
     const int wrow = wm * IT * 16, wcol = wn * JT * 16;
+    void *const gC = p.C;
+    const int64_t ldc = p.ldc, pM = p.M, pN = p.N;
 #pragma unroll
     for (int i = 0; i < IT; i++) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -590,7 +612,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, 
             const float4 v0 = *reinterpret_cast<const float4 *>(src);
             const int64_t m = m0 + wrow + i * 16 + row, n = n0 + wcol + col;
             if (OUT_PARTIAL) {
-                *reinterpret_cast<float4 *>(ws + ((int64_t)split * p.M + m) * p.N + n) = v0;
+                *reinterpret_cast<float4 *>(ws + ((int64_t)split * pM + m) * pN + n) = v0;
             } else if (CBF16) {
                 const float4 v1 = *reinterpret_cast<const float4 *>(src + 4);
                 uint4 o;
@@ -598,12 +620,55 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, 
                 o.y = (uint32_t)to_bf16(v0.z) | ((uint32_t)to_bf16(v0.w) << 16);
                 o.z = (uint32_t)to_bf16(v1.x) | ((uint32_t)to_bf16(v1.y) << 16);
                 o.w = (uint32_t)to_bf16(v1.z) | ((uint32_t)to_bf16(v1.w) << 16);
-                *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.C) + m * p.ldc + n) = o;
+                *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(gC) + m * ldc + n) = o;
             } else {
-                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.C) + m * p.ldc + n) = v0;
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(gC) + m * ldc + n) = v0;
             }
         }
     }
+}
+
+// Split-K: workgroup b handles K blocks [kb_lo, kb_hi) of split s = b / tiles.
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL>
+__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n,
+                                                                 int splits, float *ws)
+{
+    const int tiles = tiles_m * tiles_n;
+    const int b = xcd_contiguous(blockIdx.x, tiles * splits);
+    const int split = b / tiles;
+    int tm, tn;
+    tile_coords(b - split * tiles, tiles_m, tiles_n, tm, tn);
+    const int64_t kb_lo = p.KB * split / splits, kb_hi = p.KB * (split + 1) / splits;
+    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, OUT_PARTIAL>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN, kb_lo,
+                                                      kb_hi, split, ws);
+}
+
+// Several independent problems in one launch: problem i owns workgroups
+// [first[i], first[i+1]), one per output tile, walked as in gemm_fast_kernel.
+constexpr int kGroupMax = 16;
+struct GroupArgs {
+    GemmArgs p[kGroupMax];
+    int first[kGroupMax + 1];
+    int count;
+};
+
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
+__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_group_kernel(GroupArgs g)
+{
+    const int b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < g.count && b >= g.first[i + 1])
+        i++;
+    // i is the same in every lane: say so, so that the problem's fields are
+    // read with scalar loads and kept in scalar registers
+    i = __builtin_amdgcn_readfirstlane(i);
+    const GemmArgs &p = g.p[i];
+    const int tiles_m = (int)(p.M / Cfg::TM), tiles_n = (int)(p.N / Cfg::TN);
+    const int t = xcd_contiguous(b - g.first[i], tiles_m * tiles_n);
+    int tm, tn;
+    tile_coords(t, tiles_m, tiles_n, tm, tn);
+    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, false>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN, 0, p.KB, 0,
+                                                 nullptr);
 }
 
 // C[m][n] = sum over s = 0 .. splits-1, in that order, of ws[s][m][n]; four
@@ -728,20 +793,8 @@ hipError_t launch_layout(const GemmProblem &p, const GemmArgs &a, float *ws, hip
     return p.c_bf16 ? launch_one<LAYOUT, 0, true>(a, ws, st) : launch_one<LAYOUT, 0, false>(a, ws, st);
 }
 
-} // namespace
-
-size_t gemm_workspace_bytes(const GemmProblem &p)
+GemmArgs make_args(const GemmProblem &p)
 {
-    const FastPlan plan = fast_plan(p.M, p.N, p.K);
-    if (!plan.ok || plan.splits == 1)
-        return 0;
-    return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
-}
-
-hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st)
-{
-    if (p.M == 0 || p.N == 0)
-        return hipSuccess;
     GemmArgs a;
     a.A = p.A;
     a.B = p.B;
@@ -756,11 +809,118 @@ hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st)
     a.ldc = p.ldc;
     a.KB = (p.K + 127) / 128;
     a.NB = (p.N + 127) / 128;
+    return a;
+}
+
+// Estimated time (us) of a whole group on one configuration, with the step
+// times of fast_plan and the group's mean K blocks per tile.
+double group_estimate(int cfg, const std::vector<GemmArgs> &ps)
+{
+    const int TM = cfg == CFG_L ? CfgL::TM : CfgQ::TM, TN = cfg == CFG_L ? CfgL::TN : CfgQ::TN;
+    double tiles = 0.0, steps = 0.0;
+    for (const GemmArgs &a : ps) {
+        const double t = (double)(a.M / TM) * (double)(a.N / TN);
+        tiles += t;
+        steps += t * (double)a.KB;
+    }
+    const double per_cu = std::ceil(tiles / kComputeUnits), mean = steps / tiles;
+    if (cfg == CFG_L)
+        return per_cu * mean * 4.4 + 5.0;
+    return std::floor(per_cu / 2.0) * mean * 2.3 + std::fmod(per_cu, 2.0) * mean * 1.8;
+}
+
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_group_cfg(const std::vector<GemmArgs> &ps, hipStream_t st)
+{
+    for (size_t lo = 0; lo < ps.size(); lo += kGroupMax) {
+        GroupArgs g;
+        g.count = (int)std::min(ps.size() - lo, (size_t)kGroupMax);
+        g.first[0] = 0;
+        for (int i = 0; i < g.count; i++) {
+            g.p[i] = ps[lo + i];
+            g.first[i + 1] = g.first[i] + (int)((g.p[i].M / Cfg::TM) * (g.p[i].N / Cfg::TN));
+        }
+        hipLaunchKernelGGL((gemm_group_kernel<Cfg, LAYOUT, BGRAN, CBF16>), dim3((unsigned)g.first[g.count]),
+                           dim3(Cfg::THREADS), 0, st, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+template <int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
+{
+    // Problems whose extents are multiples of 128 share grouped launches
+    // (longest K first, so that the longest tiles start first); any other
+    // non-empty problem runs on its own through the bounds-checked kernel.
+    std::vector<GemmArgs> fast;
+    bool all_l = true;
+    for (int i = 0; i < count; i++) {
+        const GemmProblem &p = probs[i];
+        if (p.M == 0 || p.N == 0)
+            continue;
+        if (p.K > 0 && p.K % 128 == 0 && p.M % CfgQ::TM == 0 && p.N % CfgQ::TN == 0) {
+            fast.push_back(make_args(p));
+            all_l = all_l && p.M % CfgL::TM == 0 && p.N % CfgL::TN == 0;
+        } else {
+            const GemmArgs a = make_args(p);
+            const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+            hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    if (fast.empty())
+        return hipSuccess;
+    std::stable_sort(fast.begin(), fast.end(), [](const GemmArgs &x, const GemmArgs &y) { return x.KB > y.KB; });
+    return launch_group_cfg<CfgQ, LAYOUT, BGRAN, CBF16>(fast, st);
+}
+
+template <int LAYOUT>
+hipError_t launch_group_layout(const GemmProblem *probs, int count, hipStream_t st)
+{
+    const GemmProblem &p = probs[0];
+    if (p.bgran)
+        return p.c_bf16 ? launch_group_t<LAYOUT, 1, true>(probs, count, st)
+                        : launch_group_t<LAYOUT, 1, false>(probs, count, st);
+    return p.c_bf16 ? launch_group_t<LAYOUT, 0, true>(probs, count, st)
+                    : launch_group_t<LAYOUT, 0, false>(probs, count, st);
+}
+
+} // namespace
+
+size_t gemm_workspace_bytes(const GemmProblem &p)
+{
+    const FastPlan plan = fast_plan(p.M, p.N, p.K);
+    if (!plan.ok || plan.splits == 1)
+        return 0;
+    return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+}
+
+hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st)
+{
+    if (p.M == 0 || p.N == 0)
+        return hipSuccess;
+    const GemmArgs a = make_args(p);
     float *ws = reinterpret_cast<float *>(workspace);
     switch (p.layout) {
     case 0: return launch_layout<0>(p, a, ws, st);
     case 1: return launch_layout<1>(p, a, ws, st);
     default: return launch_layout<2>(p, a, ws, st);
+    }
+}
+
+hipError_t launch_gemm_group(const GemmProblem *probs, int count, hipStream_t st)
+{
+    if (count <= 0)
+        return hipSuccess;
+    switch (probs[0].layout) {
+    case 0: return launch_group_layout<0>(probs, count, st);
+    case 1: return launch_group_layout<1>(probs, count, st);
+    default: return launch_group_layout<2>(probs, count, st);
     }
 }
 

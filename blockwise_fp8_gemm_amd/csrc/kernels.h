@@ -36,5 +36,8 @@ struct GemmProblem {
 
 size_t gemm_workspace_bytes(const GemmProblem &p);
 hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st);
+// Independent problems sharing layout, B-scale granularity and output dtype;
+// needs no workspace.
+hipError_t launch_gemm_group(const GemmProblem *probs, int count, hipStream_t st);
 
 } // namespace puro

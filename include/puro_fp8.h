@@ -158,6 +158,40 @@ puro_status_t puro_fp8_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t 
                             puro_dtype_t cdt, int64_t ldc, void *workspace, size_t ws_bytes,
                             hipStream_t stream);
 
+/*
+ * One problem of a grouped GEMM: the operands of one puro_fp8_gemm call (same
+ * meaning, storage and rules), without the shared layout, granularity and
+ * output type.
+ */
+typedef struct {
+    int64_t M, N, K;
+    const uint8_t *A;
+    int64_t lda;
+    const float *sA;
+    const uint8_t *B;
+    int64_t ldb;
+    const float *sB;
+    void *C;
+    int64_t ldc;
+} puro_gemm_desc_t;
+
+/*
+ * Grouped GEMM: `count` independent problems that share layout, B-scale
+ * granularity and output dtype, computed as by puro_fp8_gemm for each, in as
+ * few launches as possible (the problems' tiles run side by side, which fills
+ * the GPU where single small problems cannot -- e.g. the q, k and v
+ * projections of one input, or all weight gradients of a layer).
+ *   problems  HOST array of `count` descriptors, read before the call returns;
+ *             the device buffers they point to follow the rules of
+ *             puro_fp8_gemm.  No output may overlap another problem's output
+ *             or any input.
+ *   count     0 .. 4096 (0: nothing is enqueued).
+ * Needs no workspace.  Every problem is validated before anything is
+ * enqueued; the first failing problem's status is returned.
+ */
+puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                    const puro_gemm_desc_t *problems, int count, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *puro_status_string(puro_status_t status);
 

@@ -30,7 +30,8 @@ def _declared():
 def test_header_declares_the_calls():
     names = _declared()
     for n in ("puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_quant_transpose",
-              "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_status_string",
+              "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_gemm_grouped",
+              "puro_fp8_quant_dual", "puro_status_string",
               "puro_fp8_version"):
         assert n in names
 
@@ -146,6 +147,32 @@ def test_gemm_validation():
     # empty products: nothing enqueued
     assert _gemm(M=0, A=NUL, sA=NUL, C=NUL) == OK
     assert _gemm(N=0, B=NUL, sB=NUL, C=NUL, ldb=256, ldc=0) == OK
+
+
+def _grouped(descs, count=None, layout=0, bg=1, cdt=1, arr=True):
+    n = len(descs)
+    a = (pf.GemmDesc * max(n, 1))(*descs) if arr else None
+    return pf.lib().puro_fp8_gemm_grouped(layout, bg, cdt, a, n if count is None else count, None)
+
+
+def _desc(M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, C=P, ldc=256):
+    return pf.GemmDesc(M, N, K, A, lda, sA, B, ldb, sB, C, ldc)
+
+
+def test_gemm_grouped_validation():
+    assert _grouped([]) == OK                                  # nothing to do
+    assert _grouped([], layout=5) == ENUM
+    assert _grouped([], cdt=3) == ENUM
+    assert _grouped([_desc()], count=-1) == SHAPE
+    assert _grouped([_desc()], count=4097) == SHAPE
+    assert _grouped([_desc()], arr=False, count=1) == NULL
+    assert _grouped([_desc()], bg=4) == ENUM
+    assert _grouped([_desc(), _desc(ldc=128)]) == SHAPE       # the second problem fails
+    assert _grouped([_desc(A=NUL), _desc()]) == NULL
+    assert _grouped([_desc(), _desc(C=P_ODD)]) == ALIGN
+    assert _grouped([_desc(), _desc(lda=264)]) == ALIGN
+    # only empty problems: nothing enqueued
+    assert _grouped([_desc(M=0, A=NUL, sA=NUL, C=NUL), _desc(N=0, B=NUL, sB=NUL, C=NUL, ldc=0)]) == OK
 
 
 def test_workspace_size_is_defined_for_every_layout():

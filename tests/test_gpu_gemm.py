@@ -68,12 +68,14 @@ def _elem_bound(layout, bgran, qa, sa, qb, sb, K):
     return ((K + 127) // 128 + 4) * 2.0 ** -23 * c_abs
 
 
-def _check_product(layout, bgran, hostops, devops, out):
+def _check_product(layout, bgran, hostops, devops, out, C=None):
+    """Compare C (computed here by puro_fp8_gemm unless given) with the oracle."""
     qa, sa, qb, sb = hostops
     C_ref = oracle.gemm(layout, qa, sa, qb, sb, bgran)
     K = qa.shape[0] if layout == "TN" else qa.shape[1]
     E = _elem_bound(layout, bgran, qa, sa, qb, sb, K)
-    C = pf.puro_fp8_gemm(layout, *devops[:2], *devops[2:], bgran=bgran, out_dtype=out)
+    if C is None:
+        C = pf.puro_fp8_gemm(layout, *devops[:2], *devops[2:], bgran=bgran, out_dtype=out)
     torch.cuda.synchronize()
     if out == torch.float32:
         got = host(C).astype(np.float64)
@@ -208,3 +210,54 @@ def test_every_code_decodes_exactly(dev):
     np.testing.assert_array_equal(host(C)[:, 0].astype(np.float64), want)
     np.testing.assert_array_equal(host(C2)[0, :].astype(np.float64), want)
     assert (host(C)[:, 1:] == host(C)[:, :1]).all()
+
+
+# Grouped launches: aligned problems (extents multiples of 128) share launches,
+# the others (ragged, K tail) run on their own; empty ones are skipped.
+GROUP = [(256, 384, 512), (200, 136, 300), (0, 128, 256), (128, 128, 1024), (128, 128, 200),
+         (512, 256, 768), (384, 128, 128)]
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("bgran", ["1x128", "128x128"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_grouped_matches_oracle(dev, layout, bgran, out):
+    ops = []
+    for i, (M, N, K) in enumerate(GROUP):
+        X = synth.normal((M, K), 1.0, 3000 + i)
+        W = synth.normal((N, K), 0.02, 3100 + i)
+        ops.append(_quantise_both(layout, bgran, X, W, ldx=_pad(K), ldw=_pad(K)))
+    Cs = pf.puro_fp8_gemm_grouped(layout, [dv for _, dv in ops], bgran=bgran, out_dtype=out)
+    for (hostops, devops), C in zip(ops, Cs):
+        if C.numel():
+            _check_product(layout, bgran, hostops, devops, out, C=C)
+
+
+def test_grouped_more_problems_than_one_launch(dev):
+    # 21 aligned problems (more than one launch holds) with mixed K
+    ops = []
+    for i in range(21):
+        M, N, K = 128 * (1 + i % 3), 128 * (1 + i % 2), 128 * (1 + i % 5)
+        X = synth.normal((M, K), 1.0, 3200 + i)
+        W = synth.normal((N, K), 0.02, 3300 + i)
+        ops.append(_quantise_both("NT", "128x128", X, W))
+    Cs = pf.puro_fp8_gemm_grouped("NT", [dv for _, dv in ops], bgran="128x128", out_dtype=torch.float32)
+    for (hostops, devops), C in zip(ops, Cs):
+        _check_product("NT", "128x128", hostops, devops, torch.float32, C=C)
+
+
+def test_grouped_layer_projections_reduced_tokens(dev):
+    # the q, k, v projections of one input and the gate/up pair, 512 tokens:
+    # grouped forward products equal the single calls' to the parity bound
+    T = 512
+    for names in (("q", "k", "v"), ("gate", "up")):
+        gemms = [g for g in synth.LAYER_GEMMS if g[0] in names]
+        K = gemms[0][2]
+        X = synth.normal((T, K), 1.0, 3400 + K)
+        ops = []
+        for j, (g, n, k, src) in enumerate(gemms):
+            W = synth.normal((n, k), 0.02, 3500 + j)
+            ops.append(_quantise_both("NT", "128x128", X, W))
+        Cs = pf.puro_fp8_gemm_grouped("NT", [dv for _, dv in ops], out_dtype=torch.bfloat16)
+        for (hostops, devops), C in zip(ops, Cs):
+            _check_product("NT", "128x128", hostops, devops, torch.bfloat16, C=C)
