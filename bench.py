@@ -183,6 +183,57 @@ def cpu_baseline(rows):
                       % (rows, rows, rows, flops / 1e9, t_total)}
 
 
+# Measured HBM traffic per launch of each GEMM kind (rocprofv3 FETCH_SIZE and
+# WRITE_SIZE, scaled by the same counters on a plain copy of known size).  It
+# holds only for the kernel source it was measured on, identified by hash.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_fp8_gemm_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of kind `name` from TRAFFIC_FILE, or None when the
+    file is missing, has no row for it, or was measured on other kernel source."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(r"^\| `%s` \|[^\n]*\| ([0-9.eE+]+) \|\s*$" % re.escape(name), text, flags=re.M)
+    return float(m.group(1)) if m else None
+
+
+def traffic_probe():
+    """One layer of the step, three times, then a plain 1 GiB copy three times
+    (the calibration for the memory counters); run under rocprofv3 --pmc."""
+    import torch
+    import blockwise_fp8_gemm_amd as pf
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    import synth
+    plan, keep = build_stack_plan(pf, torch, dev, 1, synth.TOKENS, sp)
+    for _ in range(3):
+        plan.run()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("traffic probe done: 1 layer x 3, then copy of %d bytes x 3" % src.numel(), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,7 +242,12 @@ def main():
     ap.add_argument("--layers", type=int, default=28, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-rows", type=int, default=16, help="rows per GEMM in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run one layer and a calibration copy for the memory counters, then exit")
     args = ap.parse_args()
+    if args.traffic_probe:
+        traffic_probe()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -264,7 +320,8 @@ def main():
     if dom[1] > 0:
         achieved = dom[1] / dom[0] / 1e9            # TFLOP/s
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(dom_name),
                     "kernel": dom_name, "avg_launch_us": round(dom[0] / dom[3] * 1e3, 2)}
     else:
         achieved = dom[2] / dom[0] / 1e6            # GB/s
