@@ -8,7 +8,9 @@ the timed region: weights in 128x128 tiles, and each layer input X and each
 output gradient dY quantised both ways in one read (1x128 along features for
 the forward / data-gradient GEMM, 128-token blocks for the weight gradient).
 Products that a training step can run together share grouped launches
-(q/k/v, gate/up, and a layer's seven weight gradients).  Shapes come from the
+(q/k/v, gate/up, and a layer's seven weight gradients); the data gradients of
+the q/k/v and of the gate/up projections are summed into their input's
+gradient in one pass.  Shapes come from the
 Puro-2B-Base model card (Qwen3-1.7B configuration: hidden 2,048, FFN 6,144,
 16 / 8 heads, 28 layers; sequence length 4,096, micro-batch 2).
 
@@ -80,7 +82,7 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     qw = {g: torch.empty((n, k), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     sw = {g: torch.empty((nb(n), nb(k)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     y = {g: torch.empty((tokens, n), dtype=bf16, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    dx = {g: torch.empty((tokens, k), dtype=bf16, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
+    dx = {name: torch.empty((tokens, c), dtype=bf16, device=dev) for name, c in synth.LAYER_INPUTS}
     dw = {g: torch.empty((n, k), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, y, dx, dw]
 
@@ -97,15 +99,17 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
 
     def fwd(g):
         n, k, src = shape[g]
-        return pf.GemmDesc(T, n, k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]), P(y[g]), n)
+        return pf.gemm_desc(T, n, [(k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]))], P(y[g]), n)
 
-    def dgrad(g):
-        n, k, src = shape[g]
-        return pf.GemmDesc(T, k, n, P(qdy[g]), n, P(sdy[g]), P(qw[g]), k, P(sw[g]), P(dx[g]), k)
+    def dgrad_sum(gs):
+        # dX of one input = sum over the projections reading it of dY_g W_g
+        k, src = shape[gs[0]][1], shape[gs[0]][2]
+        segs = [(shape[g][0], P(qdy[g]), shape[g][0], P(sdy[g]), P(qw[g]), k, P(sw[g])) for g in gs]
+        return pf.gemm_desc(T, k, segs, P(dx[src]), k)
 
     def wgrad(g):
         n, k, src = shape[g]
-        return pf.GemmDesc(n, k, T, P(qdyt[g]), T, P(sdyt[g]), P(qxt[src]), T, P(sxt[src]), P(dw[g]), k)
+        return pf.gemm_desc(n, k, [(T, P(qdyt[g]), T, P(sdyt[g]), P(qxt[src]), T, P(sxt[src]))], P(dw[g]), k)
 
     def fl(gs):
         return sum(2.0 * T * shape[g][0] * shape[g][1] for g in gs)
@@ -113,7 +117,9 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     # Products that can run together share one grouped launch, in the order a
     # training step allows: the q, k and v projections of one input, the gate
     # and up projections of one input; backward from the last projection to
-    # the first; the weight gradients of a layer once its output gradients exist.
+    # the first, the data gradients of projections that read the same input
+    # summed into that input's gradient in one pass (K segments); the weight
+    # gradients of a layer once its output gradients exist.
     FWD_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
     DGRAD_GROUPS = (("down",), ("gate", "up"), ("o",), ("q", "k", "v"))
     for layer in range(layers):
@@ -144,7 +150,7 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
                                              P(sdyt[g]), stream_ptr),
                      "quant_dual", "quant_dual", 0, T * n * (2 + 2 + 8 / 128))
         for gs in DGRAD_GROUPS:
-            grouped(NN, S128, BF16, [dgrad(g) for g in gs], "gemm_dgrad_NN_128x128_bf16", fl(gs))
+            grouped(NN, S128, BF16, [dgrad_sum(gs)], "gemm_dgrad_NN_128x128_bf16", fl(gs))
         gs = [g for g, _, _, _ in synth.LAYER_GEMMS]
         grouped(NT, S1, F32, [wgrad(g) for g in gs], "gemm_wgrad_NT_1x128_f32", fl(gs))
     return plan, keep

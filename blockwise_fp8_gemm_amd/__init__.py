@@ -38,12 +38,30 @@ class PuroError(RuntimeError):
         super().__init__("%s failed: %s (status %d)" % (what, puro_status_string(status), status))
 
 
+class GemmSegment(ctypes.Structure):
+    """puro_gemm_segment_t: one K segment of a grouped-GEMM problem."""
+    _fields_ = [("K", ctypes.c_int64), ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("sA", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("sB", ctypes.c_void_p)]
+
+
+MAX_SEGMENTS = 4
+
+
 class GemmDesc(ctypes.Structure):
     """puro_gemm_desc_t: one problem of puro_fp8_gemm_grouped."""
-    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("sA", ctypes.c_void_p),
-                ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("sB", ctypes.c_void_p),
-                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("nseg", ctypes.c_int), ("accumulate", ctypes.c_int),
+                ("seg", GemmSegment * MAX_SEGMENTS), ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
+
+
+def gemm_desc(M, N, segments, C, ldc, accumulate=False):
+    """GemmDesc from (K, A, lda, sA, B, ldb, sB) tuples of pointers and strides."""
+    if not 1 <= len(segments) <= MAX_SEGMENTS:
+        raise ValueError("1 to %d segments" % MAX_SEGMENTS)
+    d = GemmDesc()
+    d.M, d.N, d.nseg, d.accumulate, d.C, d.ldc = M, N, len(segments), int(bool(accumulate)), C, ldc
+    for i, g in enumerate(segments):
+        d.seg[i] = GemmSegment(*g)
+    return d
 
 
 def lib():
@@ -279,26 +297,40 @@ def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat1
 
 
 def gemm_descs(layout, problems, bgran="128x128", out_dtype=torch.bfloat16):
-    """Checked descriptors for puro_fp8_gemm_grouped.  problems: a list of
-    (A, sA, B, sB) or (A, sA, B, sB, C); missing outputs are allocated.
+    """Checked descriptors for puro_fp8_gemm_grouped.  Each problem is
+    (A, sA, B, sB), (A, sA, B, sB, C), or a dict with "segments" (a list of
+    (A, sA, B, sB) summed into one output), optional "C" and "accumulate"
+    (C += the sum instead of C = the sum).  Missing outputs are allocated.
     Returns (ctypes array of GemmDesc, list of C)."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype is float32 or bfloat16")
     descs = (GemmDesc * max(len(problems), 1))()
     outs = []
     for i, prob in enumerate(problems):
-        A, sA, B, sB = prob[:4]
-        C = prob[4] if len(prob) > 4 else None
-        M, N, K = gemm_dims(layout, A, B)
-        if A.dtype != torch.uint8 or B.dtype != torch.uint8:
-            raise TypeError("A and B hold E4M3 codes (torch.uint8)")
-        sa_shape, sb_shape = scale_shapes(layout, bgran, M, N, K)
-        _need_dense(sA, sa_shape, "sA")
-        _need_dense(sB, sb_shape, "sB")
+        if isinstance(prob, dict):
+            segs, C, acc = prob["segments"], prob.get("C"), prob.get("accumulate", False)
+        else:
+            segs, C, acc = [prob[:4]], (prob[4] if len(prob) > 4 else None), False
+        if acc and C is None:
+            raise ValueError("accumulate needs C")
+        MN = None
+        raw = []
+        for A, sA, B, sB in segs:
+            M, N, K = gemm_dims(layout, A, B)
+            if MN is not None and (M, N) != MN:
+                raise ValueError("segments of one problem share M and N")
+            MN = (M, N)
+            if A.dtype != torch.uint8 or B.dtype != torch.uint8:
+                raise TypeError("A and B hold E4M3 codes (torch.uint8)")
+            sa_shape, sb_shape = scale_shapes(layout, bgran, M, N, K)
+            _need_dense(sA, sa_shape, "sA")
+            _need_dense(sB, sb_shape, "sB")
+            raw.append((K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB)))
+        M, N = MN
         if C is None:
-            C = empty_2d(M, N, out_dtype, A.device)
+            C = empty_2d(M, N, out_dtype, segs[0][0].device)
         _need(C, (M, N), out_dtype, "C")
-        descs[i] = GemmDesc(M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), _ptr(C), _ld(C))
+        descs[i] = gemm_desc(M, N, raw, _ptr(C), _ld(C), acc)
         outs.append(C)
     return descs, outs
 

@@ -170,15 +170,13 @@ static puro::GemmProblem make_problem(puro_layout_t layout, int64_t M, int64_t N
     p.layout = (int)layout;
     p.bgran = (int)bgran;
     p.c_bf16 = cdt == PURO_BF16;
+    p.accumulate = false;
     p.M = M;
     p.N = N;
-    p.K = K;
-    p.A = A;
-    p.lda = lda;
-    p.sA = sA;
-    p.B = B;
-    p.ldb = ldb;
-    p.sB = sB;
+    p.nseg = 1;
+    p.seg[0] = puro::GemmSegment{K, A, lda, sA, B, ldb, sB};
+    for (int i = 1; i < puro::kGemmMaxSeg; i++)
+        p.seg[i] = puro::GemmSegment{0, nullptr, 0, nullptr, nullptr, 0, nullptr};
     p.C = C;
     p.ldc = ldc;
     return p;
@@ -233,12 +231,23 @@ puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, p
         ps.reserve((size_t)count);
         for (int i = 0; i < count; i++) {
             const puro_gemm_desc_t &d = problems[i];
-            const puro_status_t st = check_gemm(layout, d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB,
-                                                bgran, d.C, cdt, d.ldc);
-            if (st != PURO_OK)
-                return st;
-            ps.push_back(make_problem(layout, d.M, d.N, d.K, d.A, d.lda, d.sA, d.B, d.ldb, d.sB, bgran, d.C,
-                                      cdt, d.ldc));
+            if (d.nseg < 1 || d.nseg > PURO_GEMM_MAX_SEGMENTS)
+                return PURO_ERR_SHAPE;
+            if (d.accumulate != 0 && d.accumulate != 1)
+                return PURO_ERR_ENUM;
+            puro::GemmProblem p = make_problem(layout, d.M, d.N, 0, nullptr, 0, nullptr, nullptr, 0, nullptr,
+                                               bgran, d.C, cdt, d.ldc);
+            for (int j = 0; j < d.nseg; j++) {
+                const puro_gemm_segment_t &g = d.seg[j];
+                const puro_status_t st = check_gemm(layout, d.M, d.N, g.K, g.A, g.lda, g.sA, g.B, g.ldb, g.sB,
+                                                    bgran, d.C, cdt, d.ldc);
+                if (st != PURO_OK)
+                    return st;
+                p.seg[j] = puro::GemmSegment{g.K, g.A, g.lda, g.sA, g.B, g.ldb, g.sB};
+            }
+            p.nseg = d.nseg;
+            p.accumulate = d.accumulate == 1;
+            ps.push_back(p);
         }
         if (layout != PURO_NT && layout != PURO_NN && layout != PURO_TN)
             return PURO_ERR_ENUM;

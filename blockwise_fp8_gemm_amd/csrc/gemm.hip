@@ -45,14 +45,26 @@ namespace puro {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int kMaxKSeg = kGemmMaxSeg;
 
-struct GemmArgs {
+// One K segment of a product: A, B and their scales over K indices 0 .. K-1.
+struct KSeg {
     const uint8_t *A;
     const uint8_t *B;
     const float *sA;
     const float *sB;
+    int64_t K, lda, ldb, KB;
+};
+
+// C (+)= sum over the segments of each segment's blockwise product; the
+// segments share M, N and the output, and are accumulated in FP32 before the
+// single rounding of the output.
+struct GemmArgs {
+    KSeg seg[kMaxKSeg];
+    int nseg;
+    int accumulate;   // 0: C = sum; 1: C = C + sum
     void *C;
-    int64_t M, N, K, lda, ldb, ldc, KB, NB;
+    int64_t M, N, ldc, NB;
 };
 
 // Stage a 128 x 128-byte tile of a row-major byte matrix into LDS.
@@ -178,17 +190,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
     for (int j = 0; j < 4; j++)
         ncol[j] = n0 + wn * 64 + j * 16 + (lane & 15);
 
-    for (int64_t kb = 0; kb < p.KB; kb++) {
+    for (int sgi = 0; sgi < p.nseg; sgi++)
+    for (int64_t kb = 0; kb < p.seg[sgi].KB; kb++) {
+        const KSeg &sg = p.seg[sgi];
         const int64_t k0 = kb * BK;
         __syncthreads();
         if (A_KMAJ)
-            stage_tile<true>(lds_a, p.A, p.lda, m0, p.M, k0, p.K, tid);
+            stage_tile<true>(lds_a, sg.A, sg.lda, m0, p.M, k0, sg.K, tid);
         else
-            stage_tile<false>(lds_a, p.A, p.lda, k0, p.K, m0, p.M, tid);
+            stage_tile<false>(lds_a, sg.A, sg.lda, k0, sg.K, m0, p.M, tid);
         if (B_KMAJ)
-            stage_tile<true>(lds_b, p.B, p.ldb, n0, p.N, k0, p.K, tid);
+            stage_tile<true>(lds_b, sg.B, sg.ldb, n0, p.N, k0, sg.K, tid);
         else
-            stage_tile<false>(lds_b, p.B, p.ldb, k0, p.K, n0, p.N, tid);
+            stage_tile<false>(lds_b, sg.B, sg.ldb, k0, sg.K, n0, p.N, tid);
         __syncthreads();
 
         // Scales of this K block for this lane's rows and columns.
@@ -198,7 +212,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int64_t m = mrow[i][r];
-                sa[i][r] = (m < p.M) ? (A_KMAJ ? p.sA[m * p.KB + kb] : p.sA[kb * p.M + m]) : 0.0f;
+                sa[i][r] = (m < p.M) ? (A_KMAJ ? sg.sA[m * sg.KB + kb] : sg.sA[kb * p.M + m]) : 0.0f;
             }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -206,9 +220,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
             float v = 0.0f;
             if (n < p.N) {
                 if (LAYOUT == 0)
-                    v = BGRAN ? p.sB[(n >> 7) * p.KB + kb] : p.sB[n * p.KB + kb];
+                    v = BGRAN ? sg.sB[(n >> 7) * sg.KB + kb] : sg.sB[n * sg.KB + kb];
                 else
-                    v = BGRAN ? p.sB[kb * p.NB + (n >> 7)] : p.sB[kb * p.N + n];
+                    v = BGRAN ? sg.sB[kb * p.NB + (n >> 7)] : sg.sB[kb * p.N + n];
             }
             sb[j] = v;
         }
@@ -247,10 +261,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
                 const int64_t n = ncol[j];
                 if (n >= p.N)
                     continue;
-                if (CBF16)
-                    reinterpret_cast<uint16_t *>(p.C)[m * p.ldc + n] = to_bf16(acc[i][j][r]);
-                else
-                    reinterpret_cast<float *>(p.C)[m * p.ldc + n] = acc[i][j][r];
+                if (CBF16) {
+                    uint16_t *c = reinterpret_cast<uint16_t *>(p.C) + m * p.ldc + n;
+                    *c = to_bf16(p.accumulate ? __uint_as_float((uint32_t)*c << 16) + acc[i][j][r] : acc[i][j][r]);
+                } else {
+                    float *c = reinterpret_cast<float *>(p.C) + m * p.ldc + n;
+                    *c = p.accumulate ? *c + acc[i][j][r] : acc[i][j][r];
+                }
             }
         }
 }
@@ -400,9 +417,10 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n)
 }
 
 // One workgroup's output tile: rows [m0, m0 + TM) x columns [n0, n0 + TN) of
-// problem p, over K blocks [kb_lo, kb_hi).  With OUT_PARTIAL the FP32 result
-// goes to ws[split][M][N] (row stride N) instead of C.
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL>
+// problem p, over K blocks [kb_lo, kb_hi) numbered across its segments.  With
+// OUT_PARTIAL the FP32 result goes to ws[split][M][N] (row stride N) instead
+// of C.  MULTI: p may have more than one segment.
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, bool MULTI>
 __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t n0, int64_t kb_lo,
                                           int64_t kb_hi, int split, float *ws)
 {
@@ -429,70 +447,102 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             for (int r = 0; r < 4; r++)
                 acc[i][j][r] = 0.0f;
 
-    // The problem's operands, read once.  Scales: thread q copies, for every K
-    // block kb, the scale at sc_base + kb * sc_step: A's scale of tile row q
-    // (q < TM), then B's scales (one per tile column, or one per 128-wide
-    // weight tile), then harmless duplicates of A's first, so that every wave
-    // issues the same copies.
-    const uint8_t *const gA = p.A, *const gB = p.B;
-    const int64_t lda = p.lda, ldb = p.ldb;
-    const float *sc_base;
-    int64_t sc_step;
-    {
-        const int nsb = BGRAN ? TN / 128 : TN;
-        if (tid < TM) {
-            const int64_t m = m0 + tid;
-            sc_base = A_KMAJ ? p.sA + m * p.KB : p.sA + m;
-            sc_step = A_KMAJ ? 1 : p.M;
-        } else if (tid < TM + nsb) {
-            const int64_t q = tid - TM;
-            if (BGRAN) {
-                const int64_t nb = (n0 >> 7) + q;
-                sc_base = B_KMAJ ? p.sB + nb * p.KB : p.sB + nb;
-                sc_step = B_KMAJ ? 1 : p.NB;
-            } else {
-                const int64_t n = n0 + q;
-                sc_base = B_KMAJ ? p.sB + n * p.KB : p.sB + n;
-                sc_step = B_KMAJ ? 1 : p.N;
-            }
-        } else {
-            sc_base = A_KMAJ ? p.sA + m0 * p.KB : p.sA + m0;
-            sc_step = A_KMAJ ? 1 : p.M;
-        }
-    }
-
-    auto stage = [&](int64_t kb, int buf) {
-        const int64_t k0 = kb * 128;
-        uint8_t *ta = lds[buf];
-        uint8_t *tb = lds[buf] + A_BYTES;
-        if (A_KMAJ)
-            fast_stage_k<TM, NW>(ta, gA, lda, m0, k0, wave, lane);
-        else
-            fast_stage_mn<TM, NW>(ta, gA, lda, k0, m0, wave, lane);
-        if (B_KMAJ)
-            fast_stage_k<TN, NW>(tb, gB, ldb, n0, k0, wave, lane);
-        else
-            fast_stage_mn<TN, NW>(tb, gB, ldb, k0, n0, wave, lane);
-        load_lds4(sc_base + kb * sc_step, &lds_sc[buf][wave * 64]);
-    };
-
     // vmcnt(n) immediate for gfx9-family s_waitcnt (expcnt and lgkmcnt left unconstrained)
     constexpr int WAIT_NEWEST = 0x0F70 | (Cfg::LOADS & 15) | ((Cfg::LOADS >> 4) << 14);
     static_assert(Cfg::LOADS < 64, "vmcnt range");
 
-    for (int s = 0; s < STAGES - 1; s++)
-        if (kb_lo + s < kb_hi)
-            stage(kb_lo + s, s);
+    // K blocks are numbered across the segments, in order: block v of the
+    // product is block v - (blocks of the segments before) of its segment.
+    // Scales: thread q copies, for every K block, A's scale of tile row q
+    // (q < TM), then B's scales (one per tile column, or one per 128-wide
+    // weight tile), then harmless duplicates of A's first, so that every wave
+    // issues the same copies.
+    const int nsb = BGRAN ? TN / 128 : TN;
+    // This thread's scale source for block kb of segment sg: base + kb * step.
+    auto scale_source = [&](const KSeg &sg, const float *&base, int64_t &step) {
+        if (tid < TM) {
+            const int64_t m = m0 + tid;
+            base = A_KMAJ ? sg.sA + m * sg.KB : sg.sA + m;
+            step = A_KMAJ ? 1 : p.M;
+        } else if (tid < TM + nsb) {
+            const int64_t q = tid - TM;
+            if (BGRAN) {
+                const int64_t nb = (n0 >> 7) + q;
+                base = B_KMAJ ? sg.sB + nb * sg.KB : sg.sB + nb;
+                step = B_KMAJ ? 1 : p.NB;
+            } else {
+                const int64_t n = n0 + q;
+                base = B_KMAJ ? sg.sB + n * sg.KB : sg.sB + n;
+                step = B_KMAJ ? 1 : p.N;
+            }
+        } else {
+            base = A_KMAJ ? sg.sA + m0 * sg.KB : sg.sA + m0;
+            step = A_KMAJ ? 1 : p.M;
+        }
+    };
+    auto stage_seg = [&](const KSeg &sg, int64_t kb, const float *sc, int buf) {
+        const int64_t k0 = kb * 128;
+        uint8_t *ta = lds[buf];
+        uint8_t *tb = lds[buf] + A_BYTES;
+        if (A_KMAJ)
+            fast_stage_k<TM, NW>(ta, sg.A, sg.lda, m0, k0, wave, lane);
+        else
+            fast_stage_mn<TM, NW>(ta, sg.A, sg.lda, k0, m0, wave, lane);
+        if (B_KMAJ)
+            fast_stage_k<TN, NW>(tb, sg.B, sg.ldb, n0, k0, wave, lane);
+        else
+            fast_stage_mn<TN, NW>(tb, sg.B, sg.ldb, k0, n0, wave, lane);
+        load_lds4(sc, &lds_sc[buf][wave * 64]);
+    };
+
+    // One segment (the common case): operands and scale source fixed.
+    const KSeg seg0 = p.seg[0];
+    const float *sc0_base;
+    int64_t sc0_step;
+    scale_source(seg0, sc0_base, sc0_step);
+    // Several segments: block v belongs to the segment whose first block is
+    // the largest one <= v (a switch, so that every read of the argument block
+    // has a constant index and stays in scalar registers).
+    static_assert(kMaxKSeg == 4, "segment lookup below");
+    int64_t seg_start[4];   // first block of each segment; past-the-end ones never match
+    seg_start[0] = 0;
+    seg_start[1] = MULTI && p.nseg > 1 ? p.seg[0].KB : INT64_MAX;
+    seg_start[2] = MULTI && p.nseg > 2 ? seg_start[1] + p.seg[1].KB : INT64_MAX;
+    seg_start[3] = MULTI && p.nseg > 3 ? seg_start[2] + p.seg[2].KB : INT64_MAX;
+    auto stage = [&](int64_t v, int buf) {
+        if (!MULTI) {
+            stage_seg(seg0, v, sc0_base + v * sc0_step, buf);
+            return;
+        }
+        const int si = (v >= seg_start[1]) + (v >= seg_start[2]) + (v >= seg_start[3]);
+        KSeg sg;
+        int64_t kb;
+        switch (si) {
+        case 0: sg = p.seg[0]; kb = v; break;
+        case 1: sg = p.seg[1]; kb = v - seg_start[1]; break;
+        case 2: sg = p.seg[2]; kb = v - seg_start[2]; break;
+        default: sg = p.seg[3]; kb = v - seg_start[3]; break;
+        }
+        const float *base;
+        int64_t step;
+        scale_source(sg, base, step);
+        stage_seg(sg, kb, base + kb * step, buf);
+    };
+
+    const int64_t lo = kb_lo, hi = kb_hi;
     int buf = 0;
-    for (int64_t kb = kb_lo; kb < kb_hi; kb++) {
+    for (int s = 0; s < STAGES - 1; s++)
+        if (lo + s < hi)
+            stage(lo + s, buf + s < STAGES ? buf + s : buf + s - STAGES);
+    for (int64_t kb = lo; kb < hi; kb++) {
         // Block kb's copies must have landed.  With three stages, block
         // kb+1's copies (issued one iteration later) may still be in flight.
-        if (STAGES > 2 && kb + 1 < kb_hi)
+        if (STAGES > 2 && kb + 1 < hi)
             __builtin_amdgcn_s_waitcnt(WAIT_NEWEST);
         else
             __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();   // everyone's copies of block kb have landed; block kb-1 is no longer read
-        if (kb + STAGES - 1 < kb_hi) {
+        if (kb + STAGES - 1 < hi) {
             int nb_ = buf + STAGES - 1;
             if (nb_ >= STAGES)
                 nb_ -= STAGES;
@@ -591,6 +641,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     const int wrow = wm * IT * 16, wcol = wn * JT * 16;
     void *const gC = p.C;
     const int64_t ldc = p.ldc, pM = p.M, pN = p.N;
+    const bool accumulate = p.accumulate != 0;
 #pragma unroll
     for (int i = 0; i < IT; i++) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -614,61 +665,115 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             if (OUT_PARTIAL) {
                 *reinterpret_cast<float4 *>(ws + ((int64_t)split * pM + m) * pN + n) = v0;
             } else if (CBF16) {
-                const float4 v1 = *reinterpret_cast<const float4 *>(src + 4);
+                float4 a = v0, b = *reinterpret_cast<const float4 *>(src + 4);
+                uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(gC) + m * ldc + n);
+                if (accumulate) {   // C + sum, rounded once
+                    const uint4 c = *dst;
+                    a.x += bf16_lo(c.x); a.y += bf16_hi(c.x); a.z += bf16_lo(c.y); a.w += bf16_hi(c.y);
+                    b.x += bf16_lo(c.z); b.y += bf16_hi(c.z); b.z += bf16_lo(c.w); b.w += bf16_hi(c.w);
+                }
                 uint4 o;
-                o.x = (uint32_t)to_bf16(v0.x) | ((uint32_t)to_bf16(v0.y) << 16);
-                o.y = (uint32_t)to_bf16(v0.z) | ((uint32_t)to_bf16(v0.w) << 16);
-                o.z = (uint32_t)to_bf16(v1.x) | ((uint32_t)to_bf16(v1.y) << 16);
-                o.w = (uint32_t)to_bf16(v1.z) | ((uint32_t)to_bf16(v1.w) << 16);
-                *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(gC) + m * ldc + n) = o;
+                o.x = (uint32_t)to_bf16(a.x) | ((uint32_t)to_bf16(a.y) << 16);
+                o.y = (uint32_t)to_bf16(a.z) | ((uint32_t)to_bf16(a.w) << 16);
+                o.z = (uint32_t)to_bf16(b.x) | ((uint32_t)to_bf16(b.y) << 16);
+                o.w = (uint32_t)to_bf16(b.z) | ((uint32_t)to_bf16(b.w) << 16);
+                *dst = o;
             } else {
-                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(gC) + m * ldc + n) = v0;
+                float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(gC) + m * ldc + n);
+                float4 o = v0;
+                if (accumulate) {
+                    const float4 c = *dst;
+                    o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+                }
+                *dst = o;
             }
         }
     }
 }
 
 // Split-K: workgroup b handles K blocks [kb_lo, kb_hi) of split s = b / tiles.
+// Kernel arguments are read through the kernel-argument segment pointer (a
+// constant-address-space pointer), so that indexing into them never makes the
+// compiler copy the whole argument block into per-lane scratch memory.
+typedef __attribute__((address_space(4))) const GemmArgs *KernargGemm;
+
+__device__ __forceinline__ GemmArgs load_args(KernargGemm src)
+{
+    GemmArgs a;
+#pragma unroll
+    for (int i = 0; i < kMaxKSeg; i++) {
+        a.seg[i].A = src->seg[i].A;
+        a.seg[i].B = src->seg[i].B;
+        a.seg[i].sA = src->seg[i].sA;
+        a.seg[i].sB = src->seg[i].sB;
+        a.seg[i].K = src->seg[i].K;
+        a.seg[i].lda = src->seg[i].lda;
+        a.seg[i].ldb = src->seg[i].ldb;
+        a.seg[i].KB = src->seg[i].KB;
+    }
+    a.nseg = src->nseg;
+    a.accumulate = src->accumulate;
+    a.C = src->C;
+    a.M = src->M;
+    a.N = src->N;
+    a.ldc = src->ldc;
+    a.NB = src->NB;
+    return a;
+}
+
 template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL>
-__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs p, int tiles_m, int tiles_n,
+__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs args, int tiles_m, int tiles_n,
                                                                  int splits, float *ws)
 {
+    (void)args;   // same bytes as *kargs
+    const GemmArgs p = load_args((KernargGemm)__builtin_amdgcn_kernarg_segment_ptr());
     const int tiles = tiles_m * tiles_n;
     const int b = xcd_contiguous(blockIdx.x, tiles * splits);
     const int split = b / tiles;
     int tm, tn;
     tile_coords(b - split * tiles, tiles_m, tiles_n, tm, tn);
-    const int64_t kb_lo = p.KB * split / splits, kb_hi = p.KB * (split + 1) / splits;
-    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, OUT_PARTIAL>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN, kb_lo,
-                                                      kb_hi, split, ws);
+    // split K only for single-segment products
+    const int64_t KB = p.seg[0].KB;
+    const int64_t kb_lo = KB * split / splits, kb_hi = KB * (split + 1) / splits;
+    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, OUT_PARTIAL, false>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN,
+                                                             kb_lo, kb_hi, split, ws);
 }
 
 // Several independent problems in one launch: problem i owns workgroups
 // [first[i], first[i+1]), one per output tile, walked as in gemm_fast_kernel.
-constexpr int kGroupMax = 16;
+constexpr int kGroupMax = 8;
 struct GroupArgs {
     GemmArgs p[kGroupMax];
     int first[kGroupMax + 1];
     int count;
 };
 
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
-__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_group_kernel(GroupArgs g)
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool MULTI>
+__global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_group_kernel(GroupArgs args)
 {
+    (void)args;   // read through the argument segment pointer below
+    typedef __attribute__((address_space(4))) const GroupArgs *KernargGroup;
+    const KernargGroup gp = (KernargGroup)__builtin_amdgcn_kernarg_segment_ptr();
     const int b = blockIdx.x;
     int i = 0;
-    while (i + 1 < g.count && b >= g.first[i + 1])
+    while (i + 1 < gp->count && b >= gp->first[i + 1])
         i++;
     // i is the same in every lane: say so, so that the problem's fields are
     // read with scalar loads and kept in scalar registers
     i = __builtin_amdgcn_readfirstlane(i);
-    const GemmArgs &p = g.p[i];
+    const GemmArgs p = load_args(&gp->p[i]);
+    const int first = gp->first[i];
     const int tiles_m = (int)(p.M / Cfg::TM), tiles_n = (int)(p.N / Cfg::TN);
-    const int t = xcd_contiguous(b - g.first[i], tiles_m * tiles_n);
+    const int t = xcd_contiguous(b - first, tiles_m * tiles_n);
     int tm, tn;
     tile_coords(t, tiles_m, tiles_n, tm, tn);
-    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, false>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN, 0, p.KB, 0,
-                                                 nullptr);
+    int64_t blocks = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxKSeg; s++)
+        if (s < p.nseg)
+            blocks += p.seg[s].KB;
+    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, false, MULTI>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN, 0, blocks,
+                                                       0, nullptr);
 }
 
 // C[m][n] = sum over s = 0 .. splits-1, in that order, of ws[s][m][n]; four
@@ -777,7 +882,7 @@ hipError_t launch_fast(const GemmArgs &a, const FastPlan &plan, float *ws, hipSt
 template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_one(const GemmArgs &a, float *ws, hipStream_t st)
 {
-    const FastPlan plan = fast_plan(a.M, a.N, a.K);
+    const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K);
     if (plan.ok)
         return launch_fast<LAYOUT, BGRAN, CBF16>(a, plan, ws, st);
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
@@ -796,18 +901,28 @@ hipError_t launch_layout(const GemmProblem &p, const GemmArgs &a, float *ws, hip
 GemmArgs make_args(const GemmProblem &p)
 {
     GemmArgs a;
-    a.A = p.A;
-    a.B = p.B;
-    a.sA = p.sA;
-    a.sB = p.sB;
+    a.nseg = p.nseg;
+    for (int i = 0; i < kMaxKSeg; i++) {
+        KSeg &g = a.seg[i];
+        if (i < p.nseg) {
+            const GemmSegment &q = p.seg[i];
+            g.A = q.A;
+            g.B = q.B;
+            g.sA = q.sA;
+            g.sB = q.sB;
+            g.K = q.K;
+            g.lda = q.lda;
+            g.ldb = q.ldb;
+            g.KB = (q.K + 127) / 128;
+        } else {
+            g = KSeg{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0};
+        }
+    }
+    a.accumulate = p.accumulate ? 1 : 0;
     a.C = p.C;
     a.M = p.M;
     a.N = p.N;
-    a.K = p.K;
-    a.lda = p.lda;
-    a.ldb = p.ldb;
     a.ldc = p.ldc;
-    a.KB = (p.K + 127) / 128;
     a.NB = (p.N + 127) / 128;
     return a;
 }
@@ -821,7 +936,10 @@ double group_estimate(int cfg, const std::vector<GemmArgs> &ps)
     for (const GemmArgs &a : ps) {
         const double t = (double)(a.M / TM) * (double)(a.N / TN);
         tiles += t;
-        steps += t * (double)a.KB;
+        int64_t kb = 0;
+        for (int i = 0; i < a.nseg; i++)
+            kb += a.seg[i].KB;
+        steps += t * (double)kb;
     }
     const double per_cu = std::ceil(tiles / kComputeUnits), mean = steps / tiles;
     if (cfg == CFG_L)
@@ -840,8 +958,17 @@ hipError_t launch_group_cfg(const std::vector<GemmArgs> &ps, hipStream_t st)
             g.p[i] = ps[lo + i];
             g.first[i + 1] = g.first[i] + (int)((g.p[i].M / Cfg::TM) * (g.p[i].N / Cfg::TN));
         }
-        hipLaunchKernelGGL((gemm_group_kernel<Cfg, LAYOUT, BGRAN, CBF16>), dim3((unsigned)g.first[g.count]),
-                           dim3(Cfg::THREADS), 0, st, g);
+        // launches whose problems all have one K segment take the kernel
+        // without the segment lookup
+        bool multi = false;
+        for (int i = 0; i < g.count; i++)
+            multi = multi || g.p[i].nseg > 1;
+        if (multi)
+            hipLaunchKernelGGL((gemm_group_kernel<Cfg, LAYOUT, BGRAN, CBF16, true>),
+                               dim3((unsigned)g.first[g.count]), dim3(Cfg::THREADS), 0, st, g);
+        else
+            hipLaunchKernelGGL((gemm_group_kernel<Cfg, LAYOUT, BGRAN, CBF16, false>),
+                               dim3((unsigned)g.first[g.count]), dim3(Cfg::THREADS), 0, st, g);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -861,7 +988,10 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
         const GemmProblem &p = probs[i];
         if (p.M == 0 || p.N == 0)
             continue;
-        if (p.K > 0 && p.K % 128 == 0 && p.M % CfgQ::TM == 0 && p.N % CfgQ::TN == 0) {
+        bool k_aligned = true;
+        for (int j = 0; j < p.nseg; j++)
+            k_aligned = k_aligned && p.seg[j].K % 128 == 0;
+        if (k_aligned && p.M % CfgQ::TM == 0 && p.N % CfgQ::TN == 0) {
             fast.push_back(make_args(p));
             all_l = all_l && p.M % CfgL::TM == 0 && p.N % CfgL::TN == 0;
         } else {
@@ -875,7 +1005,14 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
     }
     if (fast.empty())
         return hipSuccess;
-    std::stable_sort(fast.begin(), fast.end(), [](const GemmArgs &x, const GemmArgs &y) { return x.KB > y.KB; });
+    auto blocks = [](const GemmArgs &x) {
+        int64_t kb = 0;
+        for (int j = 0; j < x.nseg; j++)
+            kb += x.seg[j].KB;
+        return kb;
+    };
+    std::stable_sort(fast.begin(), fast.end(),
+                     [&](const GemmArgs &x, const GemmArgs &y) { return blocks(x) > blocks(y); });
     return launch_group_cfg<CfgQ, LAYOUT, BGRAN, CBF16>(fast, st);
 }
 
@@ -894,7 +1031,7 @@ hipError_t launch_group_layout(const GemmProblem *probs, int count, hipStream_t 
 
 size_t gemm_workspace_bytes(const GemmProblem &p)
 {
-    const FastPlan plan = fast_plan(p.M, p.N, p.K);
+    const FastPlan plan = fast_plan(p.M, p.N, p.seg[0].K);
     if (!plan.ok || plan.splits == 1)
         return 0;
     return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);

@@ -19,21 +19,35 @@ hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t c
                              uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
                              int64_t ldqt, float *st, hipStream_t stream);
 
-struct GemmProblem {
-    int layout;   // 0 NT, 1 NN, 2 TN
-    int bgran;    // 0 1x128, 1 128x128
-    bool c_bf16;  // output dtype
-    int64_t M, N, K;
+constexpr int kGemmMaxSeg = 4;
+
+// One K segment of a product: A, B and their block scales over K indices 0 .. K-1.
+struct GemmSegment {
+    int64_t K;
     const uint8_t *A;
     int64_t lda;
     const float *sA;
     const uint8_t *B;
     int64_t ldb;
     const float *sB;
+};
+
+// C (+)= sum over segments of the blockwise product; the segments share M, N
+// and the output.
+struct GemmProblem {
+    int layout;   // 0 NT, 1 NN, 2 TN
+    int bgran;    // 0 1x128, 1 128x128
+    bool c_bf16;  // output dtype
+    bool accumulate;
+    int64_t M, N;
+    int nseg;
+    GemmSegment seg[kGemmMaxSeg];
     void *C;
     int64_t ldc;
 };
 
+// Single-segment, overwriting problems (accumulate and extra segments are the
+// grouped launcher's).
 size_t gemm_workspace_bytes(const GemmProblem &p);
 hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st);
 // Independent problems sharing layout, B-scale granularity and output dtype;

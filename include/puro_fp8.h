@@ -159,35 +159,59 @@ puro_status_t puro_fp8_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t 
                             hipStream_t stream);
 
 /*
- * One problem of a grouped GEMM: the operands of one puro_fp8_gemm call (same
- * meaning, storage and rules), without the shared layout, granularity and
- * output type.
+ * One K segment of a grouped-GEMM problem: A, B and their scales over the
+ * segment's own K indices 0 .. K-1, with the storage, scale layout and rules
+ * of puro_fp8_gemm's A, lda, sA, B, ldb, sB for (M, N, K).
  */
 typedef struct {
-    int64_t M, N, K;
+    int64_t K;
     const uint8_t *A;
     int64_t lda;
     const float *sA;
     const uint8_t *B;
     int64_t ldb;
     const float *sB;
+} puro_gemm_segment_t;
+
+#define PURO_GEMM_MAX_SEGMENTS 4
+
+/*
+ * One problem of a grouped GEMM:
+ *   C = sum over s < nseg of A_s B_s           (accumulate = 0)
+ *   C = C + sum over s < nseg of A_s B_s       (accumulate = 1)
+ * where each A_s B_s is the blockwise product of puro_fp8_gemm (blocks of
+ * 128 along each segment's own K).  The sum and the addition of the old C
+ * happen in FP32 and C is rounded once.  Several segments sum the partial
+ * products of one output (the data gradient of the q, k and v projections,
+ * dX = dY_q W_q + dY_k W_k + dY_v W_v, in one pass); accumulate adds into
+ * an existing output (weight gradients summed over micro-batches).  With
+ * accumulate = 1, C is read: it must hold finite values.
+ *   nseg        1 .. PURO_GEMM_MAX_SEGMENTS; seg[nseg ..] are ignored.
+ */
+typedef struct {
+    int64_t M, N;
+    int nseg;
+    int accumulate;
+    puro_gemm_segment_t seg[PURO_GEMM_MAX_SEGMENTS];
     void *C;
     int64_t ldc;
 } puro_gemm_desc_t;
 
 /*
  * Grouped GEMM: `count` independent problems that share layout, B-scale
- * granularity and output dtype, computed as by puro_fp8_gemm for each, in as
- * few launches as possible (the problems' tiles run side by side, which fills
- * the GPU where single small problems cannot -- e.g. the q, k and v
- * projections of one input, or all weight gradients of a layer).
+ * granularity and output dtype, in as few launches as possible (the
+ * problems' tiles run side by side, which fills the GPU where single small
+ * problems cannot -- e.g. the q, k and v projections of one input, or all
+ * weight gradients of a layer).
  *   problems  HOST array of `count` descriptors, read before the call returns;
  *             the device buffers they point to follow the rules of
  *             puro_fp8_gemm.  No output may overlap another problem's output
  *             or any input.
  *   count     0 .. 4096 (0: nothing is enqueued).
  * Needs no workspace.  Every problem is validated before anything is
- * enqueued; the first failing problem's status is returned.
+ * enqueued and the first failing problem's status is returned: nseg outside
+ * 1 .. PURO_GEMM_MAX_SEGMENTS is PURO_ERR_SHAPE, accumulate other than 0 or 1
+ * is PURO_ERR_ENUM, and every segment is checked as a puro_fp8_gemm call.
  */
 puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
                                     const puro_gemm_desc_t *problems, int count, hipStream_t stream);

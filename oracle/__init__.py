@@ -216,6 +216,22 @@ def gemm_brute(layout, A, sA, B, sB, bgran="128x128"):
     return C
 
 
+def gemm_segments(layout, segments, bgran="128x128", c_init=None):
+    """C = c_init + sum over K segments of the blockwise product, in FP64.
+
+    Each segment is (A, sA, B, sB) with its own K, blocked along its own K
+    from its first index (the segments of one output share M and N).  This is
+    the plain sum of the partial products that a linear layer's inputs
+    receive from several projections (the data gradient of an input read by
+    the q, k and v projections is dY_q W_q + dY_k W_k + dY_v W_v), and the
+    accumulate-into output used to sum weight gradients over micro-batches."""
+    out = None if c_init is None else np.array(c_init, dtype=np.float64)
+    for A, sA, B, sB in segments:
+        g = gemm(layout, A, sA, B, sB, bgran)
+        out = g if out is None else out + g
+    return out
+
+
 def bf16_rne(values):
     """FP64 -> nearest BF16 bit pattern (uint16), ties to even."""
     v = np.ascontiguousarray(values, dtype=np.float64)

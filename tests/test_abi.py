@@ -155,8 +155,10 @@ def _grouped(descs, count=None, layout=0, bg=1, cdt=1, arr=True):
     return pf.lib().puro_fp8_gemm_grouped(layout, bg, cdt, a, n if count is None else count, None)
 
 
-def _desc(M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, C=P, ldc=256):
-    return pf.GemmDesc(M, N, K, A, lda, sA, B, ldb, sB, C, ldc)
+def _desc(M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, C=P, ldc=256, nseg=1, acc=0, seg2=None):
+    d = pf.gemm_desc(M, N, [(K, A, lda, sA, B, ldb, sB)] + ([seg2] if seg2 else []), C, ldc, bool(acc))
+    d.nseg, d.accumulate = nseg if not seg2 else 2, acc
+    return d
 
 
 def test_gemm_grouped_validation():
@@ -171,6 +173,11 @@ def test_gemm_grouped_validation():
     assert _grouped([_desc(A=NUL), _desc()]) == NULL
     assert _grouped([_desc(), _desc(C=P_ODD)]) == ALIGN
     assert _grouped([_desc(), _desc(lda=264)]) == ALIGN
+    assert _grouped([_desc(nseg=0)]) == SHAPE
+    assert _grouped([_desc(nseg=5)]) == SHAPE
+    assert _grouped([_desc(acc=2)]) == ENUM
+    assert _grouped([_desc(seg2=(256, P, 128, P, P, 256, P))]) == SHAPE    # second segment's lda < K
+    assert _grouped([_desc(seg2=(256, NUL, 256, P, P, 256, P))]) == NULL
     # only empty problems: nothing enqueued
     assert _grouped([_desc(M=0, A=NUL, sA=NUL, C=NUL), _desc(N=0, B=NUL, sB=NUL, C=NUL, ldc=0)]) == OK
 

@@ -261,3 +261,75 @@ def test_grouped_layer_projections_reduced_tokens(dev):
         Cs = pf.puro_fp8_gemm_grouped("NT", [dv for _, dv in ops], out_dtype=torch.bfloat16)
         for (hostops, devops), C in zip(ops, Cs):
             _check_product("NT", "128x128", hostops, devops, torch.bfloat16, C=C)
+
+
+def _check_sum(layout, bgran, segs_host, C, out, c_old=None):
+    """C against the oracle's segment sum (plus c_old): FP32 accumulation bound over all
+    the segments' blocks, one more rounding for the addition of c_old, one BF16 rounding."""
+    C_ref = oracle.gemm_segments(layout, segs_host, bgran, c_init=c_old)
+    kb = sum(((qa.shape[0] if layout == "TN" else qa.shape[1]) + 127) // 128 for qa, _, _, _ in segs_host)
+    c_abs = sum(oracle.gemm(layout, qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), bgran)
+                for qa, sa, qb, sb in segs_host)
+    E = (kb + 4) * 2.0 ** -23 * c_abs
+    if c_old is not None:
+        E = E + 2.0 ** -23 * np.abs(c_old)
+    torch.cuda.synchronize()
+    if out == torch.float32:
+        got = host(C).astype(np.float64)
+        assert rel_frobenius(got, C_ref) <= FROB_TOL
+        bad = np.argwhere(np.abs(got - C_ref) > E)
+        assert bad.size == 0, ("element bound", tuple(bad[0]))
+    else:
+        bits = host(C)
+        got = bf16_to_f64(bits)
+        bad = np.argwhere(np.abs(got - C_ref) > E + 2.0 ** -8 * (np.abs(C_ref) + E))
+        assert bad.size == 0, ("element bound", tuple(bad[0]))
+        assert (bits == oracle.bf16_rne(C_ref)).mean() >= 0.99
+
+
+# K-segment sums: (M, N, segment K's); aligned ones take the tile kernel, the others
+# the bounds-checked one
+SUMS = [(256, 384, (256, 384)), (200, 136, (300, 72)), (128, 128, (128, 256, 128, 512)), (256, 128, (200, 128))]
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("bgran", ["1x128", "128x128"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_grouped_segment_sums_match_oracle(dev, layout, bgran, out):
+    probs, hosts = [], []
+    for i, (M, N, ks) in enumerate(SUMS):
+        hs, ds = [], []
+        for j, K in enumerate(ks):
+            X = synth.normal((M, K), 1.0, 3600 + 10 * i + j)
+            W = synth.normal((N, K), 0.02, 3700 + 10 * i + j)
+            h, d = _quantise_both(layout, bgran, X, W, ldx=_pad(K), ldw=_pad(K))
+            hs.append(h)
+            ds.append(d)
+        probs.append({"segments": ds})
+        hosts.append(hs)
+    Cs = pf.puro_fp8_gemm_grouped(layout, probs, bgran=bgran, out_dtype=out)
+    for hs, C in zip(hosts, Cs):
+        _check_sum(layout, bgran, hs, C, out)
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(256, 256, (512,)), (200, 136, (300,)), (128, 256, (256, 128))],
+                         ids=["aligned", "ragged", "two_segments"])
+def test_grouped_accumulate_into_output(dev, shape, out):
+    M, N, ks = shape
+    hs, ds = [], []
+    for j, K in enumerate(ks):
+        X = synth.normal((M, K), 1.0, 3800 + j)
+        W = synth.normal((N, K), 0.02, 3900 + j)
+        h, d = _quantise_both("NT", "1x128", X, W, ldx=_pad(K), ldw=_pad(K))
+        hs.append(h)
+        ds.append(d)
+    C = to_dev(synth.normal((M, N), 0.5, 3999, "bf16" if out == torch.bfloat16 else "f32"), ld=_pad(N))
+    # two passes, each checked against the oracle started from the output before it
+    for _ in range(2):
+        torch.cuda.synchronize()
+        prev = host(C)
+        prev = prev.astype(np.float64) if out == torch.float32 else bf16_to_f64(prev)
+        pf.puro_fp8_gemm_grouped("NT", [{"segments": ds, "C": C, "accumulate": True}], bgran="1x128",
+                                 out_dtype=out)
+        _check_sum("NT", "1x128", hs, C, out, c_old=prev)

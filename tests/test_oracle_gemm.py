@@ -158,3 +158,37 @@ def test_empty_and_k_zero():
     sb = np.zeros((3, 0), np.float32)
     C = oracle.gemm("NT", qa, sa, qb, sb, "1x128")
     assert C.shape == (4, 3) and (C == 0).all()
+
+
+# Sums over K segments (the partial products one input's gradient receives
+# from several projections, and the accumulate-into output).  Pinned by the
+# lossless pipeline: the segments of a split K range must give numpy's FP64
+# product of the whole operands, whatever the split (ragged pieces included).
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("bgran", ["1x128", "128x128"])
+@pytest.mark.parametrize("M,N,ks", [(256, 128, (256, 384)), (200, 136, (300, 72, 128)), (128, 256, (128,))])
+def test_segments_equal_the_whole_product(layout, bgran, M, N, ks):
+    segs, Xs, Ws = [], [], []
+    for i, K in enumerate(ks):
+        X = _lossless(M, K, 400 + i * 7 + K)
+        W = _lossless(N, K, 500 + i * 7 + K)
+        segs.append(_quantise_operands(layout, bgran, X, W))
+        Xs.append(X)
+        Ws.append(W)
+    C = oracle.gemm_segments(layout, segs, bgran)
+    X = np.concatenate(Xs, axis=1).astype(np.float64)
+    W = np.concatenate(Ws, axis=1).astype(np.float64)
+    ref = X @ W.T
+    denom = np.abs(X) @ np.abs(W).T + 1e-300
+    assert (np.abs(C - ref) / denom <= 1e-13).all()
+
+
+def test_segments_accumulate_onto_c_init():
+    M, N, K = 130, 128, 256
+    X = _lossless(M, K, 601)
+    W = _lossless(N, K, 602)
+    seg = _quantise_operands("NT", "128x128", X, W)
+    c0 = synth.normal((M, N), 3.0, 603).astype(np.float64)
+    C = oracle.gemm_segments("NT", [seg], "128x128", c_init=c0)
+    ref = c0 + X.astype(np.float64) @ W.astype(np.float64).T
+    np.testing.assert_allclose(C, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
