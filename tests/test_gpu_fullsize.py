@@ -133,3 +133,82 @@ def test_outlier_stress_full_size(dev):
     _check_sampled("NT", "128x128", (rqx, rsx, rqw, rsw), outs[0], K_in, 4, torch.float32)
     _check_sampled("NN", "128x128", (rqd, rsd, rqw, rsw), outs[1], N_out, 5, torch.float32)
     _check_sampled("NT", "1x128", (rqdt, rsdt, rqxt, rsxt), outs[2], T, 6, torch.float32)
+
+
+def _check_sampled_sum(layout, bgran, segs, C, seed, out):
+    """Sampled entries of a K-segment sum against the oracle (bound over all segments' blocks)."""
+    M, N = C.shape
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, SAMPLES)
+    ns = rng.integers(0, N, SAMPLES)
+    ms[:4] = [0, 0, M - 1, M - 1]
+    ns[:4] = [0, N - 1, 0, N - 1]
+    ref = np.zeros(SAMPLES)
+    ref_abs = np.zeros(SAMPLES)
+    kb = 0
+    for qa, sa, qb, sb in segs:
+        ref += oracle.gemm_entries(layout, qa, sa, qb, sb, bgran, ms, ns)
+        ref_abs += oracle.gemm_entries(layout, qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), bgran, ms, ns)
+        kb += ((qa.shape[0] if layout == "TN" else qa.shape[1]) + 127) // 128
+    E = (kb + 4) * 2.0 ** -23 * ref_abs
+    h = host(C)
+    got = bf16_to_f64(h[ms, ns]) if out == torch.bfloat16 else h[ms, ns].astype(np.float64)
+    tol = E + 2.0 ** -8 * (np.abs(ref) + E) if out == torch.bfloat16 else E
+    bad = np.flatnonzero(np.abs(got - ref) > tol)
+    assert bad.size == 0, ("entry", int(ms[bad[0]]), int(ns[bad[0]]), got[bad[0]], ref[bad[0]])
+    if out == torch.float32:
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 2e-6
+
+
+def test_layer_grouped_full_size(dev):
+    """One whole layer at 8,192 tokens in the grouped launches the benchmark times: every
+    input and output gradient quantised both ways in one read (byte-compared over the whole
+    tensors), the forward products grouped (q/k/v, o, gate/up, down), the data gradients
+    summed per input (K segments), and the seven weight gradients in one launch."""
+    T = synth.TOKENS
+    shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
+    host_q, dev_q = {}, {}
+
+    def dual(name, x):
+        d = pf.puro_fp8_quant_dual(to_dev(x), True)
+        r = oracle.quant_act(x) + oracle.quant_transpose(x, True)
+        torch.cuda.synchronize()
+        for t, ref, what in zip(d, r, ("q_row", "s_row", "q_tok", "s_tok")):
+            _same(t, ref, (name, what))
+        host_q[name], dev_q[name] = r, d
+
+    for i, (name, c) in enumerate(synth.LAYER_INPUTS):
+        dual(name, synth.normal((T, c), 1.0, synth.seed_of(4, 0, i), "bf16"))
+    for j, (g, n, k, src) in enumerate(synth.LAYER_GEMMS):
+        dual("dY_" + g, synth.normal((T, n), 1e-3, synth.seed_of(4, 0, 20 + j), "bf16"))
+        W = synth.normal((n, k), 0.02, synth.seed_of(4, 0, 10 + j))
+        qw, sw = pf.puro_fp8_quant_weight(to_dev(W))
+        rw = oracle.quant_weight(W)
+        torch.cuda.synchronize()
+        _same(qw, rw[0], ("qW", g))
+        _same(sw, rw[1], ("sW", g))
+        host_q["W_" + g], dev_q["W_" + g] = rw, (qw, sw)
+
+    seed = 10
+    for gs in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        src = shape[gs[0]][2]
+        (hqx, hsx), (dqx, dsx) = host_q[src][:2], dev_q[src][:2]
+        Ys = pf.puro_fp8_gemm_grouped("NT", [(dqx, dsx) + dev_q["W_" + g] for g in gs], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        for g, Y in zip(gs, Ys):
+            seed += 1
+            _check_sampled("NT", "128x128", (hqx, hsx) + host_q["W_" + g], Y, shape[g][1], seed, torch.bfloat16)
+    for gs in (("down",), ("gate", "up"), ("o",), ("q", "k", "v")):
+        dsegs = [dev_q["dY_" + g][:2] + dev_q["W_" + g] for g in gs]
+        hsegs = [host_q["dY_" + g][:2] + host_q["W_" + g] for g in gs]
+        (dX,) = pf.puro_fp8_gemm_grouped("NN", [{"segments": dsegs}], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        seed += 1
+        _check_sampled_sum("NN", "128x128", hsegs, dX, seed, torch.bfloat16)
+    gs = [g for g, _, _, _ in synth.LAYER_GEMMS]
+    dWs = pf.puro_fp8_gemm_grouped("NT", [dev_q["dY_" + g][2:] + dev_q[shape[g][2]][2:] for g in gs],
+                                   bgran="1x128", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for g, dW in zip(gs, dWs):
+        seed += 1
+        _check_sampled("NT", "1x128", host_q["dY_" + g][2:] + host_q[shape[g][2]][2:], dW, T, seed, torch.float32)
