@@ -48,13 +48,13 @@ def _lib():
         lib.ref_e4m3_encode.argtypes = [ctypes.c_float]
         lib.ref_e4m3_encode_array.argtypes = [_p, _i64, _p]
         lib.ref_e4m3_decode_array.argtypes = [_p, _i64, _p]
-        for name in ("ref_quant_act", "ref_quant_weight"):
+        for name in ("ref_quant_act_rule", "ref_quant_weight_rule"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
-            f.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p]
-        lib.ref_quant_transpose.restype = ctypes.c_int
-        lib.ref_quant_transpose.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
-                                            _p, _i64, _p]
+            f.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, ctypes.c_int]
+        lib.ref_quant_transpose_rule.restype = ctypes.c_int
+        lib.ref_quant_transpose_rule.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int,
+                                                 _p, _i64, _p, ctypes.c_int]
         for name in ("ref_gemm", "ref_gemm_brute"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
@@ -117,29 +117,35 @@ def e4m3_encode(values):
 
 # --------------------------------------------------------------------------- quantisers
 
-def quant_act(x):
-    """1x128 blocks along each row of x[rows][cols] -> (q uint8 [rows][cols], s f32 [rows][ceil(cols/128)])."""
+RULES = {"amax": 0, "pow2": 1}
+
+
+def quant_act(x, rule="amax"):
+    """1x128 blocks along each row of x[rows][cols] -> (q uint8 [rows][cols], s f32 [rows][ceil(cols/128)]).
+
+    rule "amax": s = fl32(amax / 448) (the recipe); "pow2": s = the smallest power of two
+    with 448 s >= amax, in [2^-127, 2^127] (the scaled matrix cores' E8M0 scales)."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty((rows, _nblk(cols)), dtype=np.float32)
-    _check(_lib().ref_quant_act(_ptr(x), _dtype_code(x), rows, cols, cols, _ptr(q), cols, _ptr(s)),
-           "quant_act")
+    _check(_lib().ref_quant_act_rule(_ptr(x), _dtype_code(x), rows, cols, cols, _ptr(q), cols, _ptr(s),
+                                     RULES[rule]), "quant_act")
     return q, s
 
 
-def quant_weight(w):
+def quant_weight(w, rule="amax"):
     """128x128 tiles of w[rows][cols] -> (q uint8 [rows][cols], s f32 [ceil(rows/128)][ceil(cols/128)])."""
     w = np.ascontiguousarray(w)
     rows, cols = w.shape
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty((_nblk(rows), _nblk(cols)), dtype=np.float32)
-    _check(_lib().ref_quant_weight(_ptr(w), _dtype_code(w), rows, cols, cols, _ptr(q), cols, _ptr(s)),
-           "quant_weight")
+    _check(_lib().ref_quant_weight_rule(_ptr(w), _dtype_code(w), rows, cols, cols, _ptr(q), cols, _ptr(s),
+                                        RULES[rule]), "quant_weight")
     return q, s
 
 
-def quant_transpose(x, transpose_out=True):
+def quant_transpose(x, transpose_out=True, rule="amax"):
     """Blocks of 128 consecutive tokens per column of x[tokens][cols].
 
     transpose_out=True : q [cols][tokens], s [cols][ceil(tokens/128)]
@@ -155,8 +161,8 @@ def quant_transpose(x, transpose_out=True):
         q = np.empty((tokens, cols), dtype=np.uint8)
         s = np.empty((_nblk(tokens), cols), dtype=np.float32)
         ldq = cols
-    _check(_lib().ref_quant_transpose(_ptr(x), _dtype_code(x), tokens, cols, cols,
-                                      1 if transpose_out else 0, _ptr(q), ldq, _ptr(s)),
+    _check(_lib().ref_quant_transpose_rule(_ptr(x), _dtype_code(x), tokens, cols, cols,
+                                           1 if transpose_out else 0, _ptr(q), ldq, _ptr(s), RULES[rule]),
            "quant_transpose")
     return q, s
 

@@ -158,6 +158,36 @@ static float ref_quant_block(const float *vals, int64_t n, uint8_t *codes)
     return s;
 }
 
+/*
+ * Power-of-two rule, a variant for the scaled matrix cores (their block
+ * scales are E8M0: powers of two 2^k, k in [-127, 127]).  The scale is the
+ * smallest power of two s = 2^k with 448 * s >= amax, k limited to that range
+ * (a zero block gets 2^-127); q_i = E4M3(x_i / s).  x_i / s is exact in FP64
+ * and, in the range that can round to a non-zero code, in FP32 as well.
+ */
+static float ref_quant_block_pow2(const float *vals, int64_t n, uint8_t *codes)
+{
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        double a = fabs((double)vals[i]);
+        if (a > amax)
+            amax = a;
+    }
+    int k = -127;
+    while (k < 127 && 448.0 * ldexp(1.0, k) < amax)
+        k++;
+    double s = ldexp(1.0, k);
+    for (int64_t i = 0; i < n; i++)
+        codes[i] = ref_e4m3_encode((float)((double)vals[i] / s));
+    return (float)s;
+}
+
+/* Scale rules: 0 = amax / 448 (the recipe), 1 = power of two (above). */
+static float ref_quant_rule(const float *vals, int64_t n, uint8_t *codes, int rule)
+{
+    return rule ? ref_quant_block_pow2(vals, n, codes) : ref_quant_block(vals, n, codes);
+}
+
 /* Status codes shared in meaning (not in code) with the library's. */
 #define REF_OK 0
 #define REF_ERR_SHAPE 2
@@ -182,8 +212,8 @@ static int64_t ref_blen(int64_t n, int64_t b)
  * 128 consecutive elements along each row.  q[rows][cols] (stride ldq),
  * s[rows][ceil(cols/128)] dense.
  */
-int ref_quant_act(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
-                  uint8_t *q, int64_t ldq, float *s)
+int ref_quant_act_rule(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                       uint8_t *q, int64_t ldq, float *s, int rule)
 {
     if (rows < 0 || cols < 0 || ldx < cols || ldq < cols)
         return REF_ERR_SHAPE;
@@ -195,7 +225,7 @@ int ref_quant_act(const void *x, int dtype, int64_t rows, int64_t cols, int64_t 
             int64_t len = ref_blen(cols, b);
             for (int64_t i = 0; i < len; i++)
                 vals[i] = ref_load(x, dtype, r * ldx + b * 128 + i);
-            s[r * nb + b] = ref_quant_block(vals, len, q + r * ldq + b * 128);
+            s[r * nb + b] = ref_quant_rule(vals, len, q + r * ldq + b * 128, rule);
         }
     }
     return REF_OK;
@@ -206,8 +236,8 @@ int ref_quant_act(const void *x, int dtype, int64_t rows, int64_t cols, int64_t 
  * (edge tiles hold what remains).  q[rows][cols] (stride ldq),
  * s[ceil(rows/128)][ceil(cols/128)] dense.
  */
-int ref_quant_weight(const void *w, int dtype, int64_t rows, int64_t cols, int64_t ldw,
-                     uint8_t *q, int64_t ldq, float *s)
+int ref_quant_weight_rule(const void *w, int dtype, int64_t rows, int64_t cols, int64_t ldw,
+                          uint8_t *q, int64_t ldq, float *s, int rule)
 {
     if (rows < 0 || cols < 0 || ldw < cols || ldq < cols)
         return REF_ERR_SHAPE;
@@ -221,7 +251,7 @@ int ref_quant_weight(const void *w, int dtype, int64_t rows, int64_t cols, int64
             for (int64_t i = 0; i < nr; i++)
                 for (int64_t j = 0; j < nc; j++)
                     vals[i * nc + j] = ref_load(w, dtype, (tr * 128 + i) * ldw + tc * 128 + j);
-            s[tr * cb + tc] = ref_quant_block(vals, nr * nc, codes);
+            s[tr * cb + tc] = ref_quant_rule(vals, nr * nc, codes, rule);
             for (int64_t i = 0; i < nr; i++)
                 for (int64_t j = 0; j < nc; j++)
                     q[(tr * 128 + i) * ldq + tc * 128 + j] = codes[i * nc + j];
@@ -238,8 +268,8 @@ int ref_quant_weight(const void *w, int dtype, int64_t rows, int64_t cols, int64
  *   transpose_out = 1: q[cols][tokens] (stride ldq), s[cols][ceil(tokens/128)]
  *   transpose_out = 0: q[tokens][cols] (stride ldq), s[ceil(tokens/128)][cols]
  */
-int ref_quant_transpose(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t ldx,
-                        int transpose_out, uint8_t *q, int64_t ldq, float *s)
+int ref_quant_transpose_rule(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t ldx,
+                             int transpose_out, uint8_t *q, int64_t ldq, float *s, int rule)
 {
     if (tokens < 0 || cols < 0 || ldx < cols)
         return REF_ERR_SHAPE;
@@ -254,7 +284,7 @@ int ref_quant_transpose(const void *x, int dtype, int64_t tokens, int64_t cols, 
             int64_t len = ref_blen(tokens, b);
             for (int64_t i = 0; i < len; i++)
                 vals[i] = ref_load(x, dtype, (b * 128 + i) * ldx + c);
-            float sc = ref_quant_block(vals, len, codes);
+            float sc = ref_quant_rule(vals, len, codes, rule);
             for (int64_t i = 0; i < len; i++) {
                 int64_t t = b * 128 + i;
                 if (transpose_out)
@@ -269,6 +299,25 @@ int ref_quant_transpose(const void *x, int dtype, int64_t tokens, int64_t cols, 
         }
     }
     return REF_OK;
+}
+
+/* The recipe's rule (amax / 448). */
+int ref_quant_act(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t *q, int64_t ldq,
+                  float *s)
+{
+    return ref_quant_act_rule(x, dtype, rows, cols, ldx, q, ldq, s, 0);
+}
+
+int ref_quant_weight(const void *w, int dtype, int64_t rows, int64_t cols, int64_t ldw, uint8_t *q, int64_t ldq,
+                     float *s)
+{
+    return ref_quant_weight_rule(w, dtype, rows, cols, ldw, q, ldq, s, 0);
+}
+
+int ref_quant_transpose(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t ldx, int transpose_out,
+                        uint8_t *q, int64_t ldq, float *s)
+{
+    return ref_quant_transpose_rule(x, dtype, tokens, cols, ldx, transpose_out, q, ldq, s, 0);
 }
 
 /* ------------------------------------------------------------------------ */
