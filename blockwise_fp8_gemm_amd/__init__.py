@@ -73,19 +73,27 @@ def lib():
                               "or __graft_entry__.build())")
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-        for name in ("puro_fp8_quant_act", "puro_fp8_quant_weight"):
+        for name in ("puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_quant_act_pow2",
+                     "puro_fp8_quant_weight_pow2"):
             f = getattr(L, name)
             f.restype = i32
             f.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
-        L.puro_fp8_quant_transpose.restype = i32
-        L.puro_fp8_quant_transpose.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
-        L.puro_fp8_quant_dual.restype = i32
-        L.puro_fp8_quant_dual.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp, vp]
+        for name in ("puro_fp8_quant_transpose", "puro_fp8_quant_transpose_pow2"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
+        for name in ("puro_fp8_quant_dual", "puro_fp8_quant_dual_pow2"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp, vp]
         L.puro_fp8_gemm_workspace_size.restype = ctypes.c_size_t
         L.puro_fp8_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i32]
-        L.puro_fp8_gemm.restype = i32
-        L.puro_fp8_gemm.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32,
-                                    i64, vp, ctypes.c_size_t, vp]
+        for name in ("puro_fp8_gemm", "puro_fp8_gemm_mx"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp, ctypes.c_size_t, vp]
+        L.puro_fp8_gemm_mx_workspace_size.restype = ctypes.c_size_t
+        L.puro_fp8_gemm_mx_workspace_size.argtypes = [i32, i64, i64, i64, i32]
         L.puro_fp8_gemm_grouped.restype = i32
         L.puro_fp8_gemm_grouped.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, vp]
         L.puro_status_string.restype = ctypes.c_char_p
@@ -166,8 +174,9 @@ def _need_dense(t, shape, name):
         raise ValueError("%s: scale arrays must be dense (contiguous)" % name)
 
 
-def puro_fp8_quant_act(x, q=None, s=None, stream=None):
-    """1x128 blocks along each row of x [rows][cols] (float32 / bfloat16)."""
+def puro_fp8_quant_act(x, q=None, s=None, stream=None, pow2=False):
+    """1x128 blocks along each row of x [rows][cols] (float32 / bfloat16).
+    pow2: power-of-two block scales (puro_fp8_quant_act_pow2)."""
     rows, cols = x.shape
     if q is None:
         q = empty_2d(rows, cols, torch.uint8, x.device)
@@ -175,13 +184,14 @@ def puro_fp8_quant_act(x, q=None, s=None, stream=None):
         s = torch.empty((rows, _nblk(cols)), dtype=torch.float32, device=x.device)
     _need(q, (rows, cols), torch.uint8, "q")
     _need_dense(s, (rows, _nblk(cols)), "s")
-    _check(lib().puro_fp8_quant_act(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
-                                    _ptr(s), _stream(stream)), "puro_fp8_quant_act")
+    fn = lib().puro_fp8_quant_act_pow2 if pow2 else lib().puro_fp8_quant_act
+    _check(fn(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q), _ptr(s), _stream(stream)),
+           "puro_fp8_quant_act")
     return q, s
 
 
-def puro_fp8_quant_weight(w, q=None, s=None, stream=None):
-    """128x128 tiles of w [rows][cols] (float32 / bfloat16)."""
+def puro_fp8_quant_weight(w, q=None, s=None, stream=None, pow2=False):
+    """128x128 tiles of w [rows][cols] (float32 / bfloat16); pow2: power-of-two scales."""
     rows, cols = w.shape
     if q is None:
         q = empty_2d(rows, cols, torch.uint8, w.device)
@@ -189,12 +199,13 @@ def puro_fp8_quant_weight(w, q=None, s=None, stream=None):
         s = torch.empty((_nblk(rows), _nblk(cols)), dtype=torch.float32, device=w.device)
     _need(q, (rows, cols), torch.uint8, "q")
     _need_dense(s, (_nblk(rows), _nblk(cols)), "s")
-    _check(lib().puro_fp8_quant_weight(_ptr(w), _dtype_code(w), rows, cols, _ld(w), _ptr(q),
-                                       _ld(q), _ptr(s), _stream(stream)), "puro_fp8_quant_weight")
+    fn = lib().puro_fp8_quant_weight_pow2 if pow2 else lib().puro_fp8_quant_weight
+    _check(fn(_ptr(w), _dtype_code(w), rows, cols, _ld(w), _ptr(q), _ld(q), _ptr(s), _stream(stream)),
+           "puro_fp8_quant_weight")
     return q, s
 
 
-def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None):
+def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None, pow2=False):
     """128-token blocks per column of x [tokens][cols].
 
     transpose_out=True : q [cols][tokens], s [cols][ceil(tokens/128)]
@@ -209,14 +220,14 @@ def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None)
         s = torch.empty(sshape, dtype=torch.float32, device=x.device)
     _need(q, qshape, torch.uint8, "q")
     _need_dense(s, sshape, "s")
-    _check(lib().puro_fp8_quant_transpose(_ptr(x), _dtype_code(x), tokens, cols, _ld(x),
-                                          1 if transpose_out else 0, _ptr(q), _ld(q), _ptr(s),
-                                          _stream(stream)), "puro_fp8_quant_transpose")
+    fn = lib().puro_fp8_quant_transpose_pow2 if pow2 else lib().puro_fp8_quant_transpose
+    _check(fn(_ptr(x), _dtype_code(x), tokens, cols, _ld(x), 1 if transpose_out else 0, _ptr(q), _ld(q),
+              _ptr(s), _stream(stream)), "puro_fp8_quant_transpose")
     return q, s
 
 
 def puro_fp8_quant_dual(x, transpose_out=True, q_row=None, s_row=None, q_tok=None, s_tok=None,
-                        stream=None):
+                        stream=None, pow2=False):
     """One read of x [tokens][cols]: the outputs of puro_fp8_quant_act(x) and of
     puro_fp8_quant_transpose(x, transpose_out).  Returns (q_row, s_row, q_tok, s_tok)."""
     tokens, cols = x.shape
@@ -234,9 +245,9 @@ def puro_fp8_quant_dual(x, transpose_out=True, q_row=None, s_row=None, q_tok=Non
     _need_dense(s_row, (tokens, _nblk(cols)), "s_row")
     _need(q_tok, qshape, torch.uint8, "q_tok")
     _need_dense(s_tok, sshape, "s_tok")
-    _check(lib().puro_fp8_quant_dual(_ptr(x), _dtype_code(x), tokens, cols, _ld(x), _ptr(q_row),
-                                     _ld(q_row), _ptr(s_row), 1 if transpose_out else 0,
-                                     _ptr(q_tok), _ld(q_tok), _ptr(s_tok), _stream(stream)),
+    fn = lib().puro_fp8_quant_dual_pow2 if pow2 else lib().puro_fp8_quant_dual
+    _check(fn(_ptr(x), _dtype_code(x), tokens, cols, _ld(x), _ptr(q_row), _ld(q_row), _ptr(s_row),
+              1 if transpose_out else 0, _ptr(q_tok), _ld(q_tok), _ptr(s_tok), _stream(stream)),
            "puro_fp8_quant_dual")
     return q_row, s_row, q_tok, s_tok
 
@@ -271,9 +282,15 @@ def puro_fp8_gemm_workspace_size(layout, M, N, K, bgran):
     return int(lib().puro_fp8_gemm_workspace_size(LAYOUTS[layout], M, N, K, BGRAN[bgran]))
 
 
+def puro_fp8_gemm_mx_workspace_size(layout, M, N, K, bgran):
+    return int(lib().puro_fp8_gemm_mx_workspace_size(LAYOUTS[layout], M, N, K, BGRAN[bgran]))
+
+
 def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat16, C=None,
-                  workspace=None, stream=None):
-    """Blockwise-scaled E4M3 GEMM; returns C [M][N] (float32 or bfloat16)."""
+                  workspace=None, stream=None, mx=False):
+    """Blockwise-scaled E4M3 GEMM; returns C [M][N] (float32 or bfloat16).
+    mx: the scaled-FP8-matrix-core variant (puro_fp8_gemm_mx: power-of-two scales,
+    extents multiples of 128)."""
     M, N, K = gemm_dims(layout, A, B)
     if A.dtype != torch.uint8 or B.dtype != torch.uint8:
         raise TypeError("A and B hold E4M3 codes (torch.uint8)")
@@ -285,14 +302,14 @@ def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat1
     if C is None:
         C = empty_2d(M, N, out_dtype, A.device)
     _need(C, (M, N), out_dtype, "C")
-    need = puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
+    need = (puro_fp8_gemm_mx_workspace_size if mx else puro_fp8_gemm_workspace_size)(layout, M, N, K, bgran)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
-    _check(lib().puro_fp8_gemm(LAYOUTS[layout], M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B),
-                               _ld(B), _ptr(sB), BGRAN[bgran], _ptr(C),
-                               PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32, _ld(C),
-                               _ptr(workspace), ws_bytes, _stream(stream)), "puro_fp8_gemm")
+    fn = lib().puro_fp8_gemm_mx if mx else lib().puro_fp8_gemm
+    _check(fn(LAYOUTS[layout], M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), BGRAN[bgran],
+              _ptr(C), PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32, _ld(C), _ptr(workspace),
+              ws_bytes, _stream(stream)), "puro_fp8_gemm_mx" if mx else "puro_fp8_gemm")
     return C
 
 

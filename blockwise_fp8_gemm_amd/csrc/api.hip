@@ -52,11 +52,8 @@ puro_status_t from_hip(hipError_t e)
 
 } // namespace
 
-extern "C" {
-
-puro_status_t puro_fp8_quant_act(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols,
-                                 int64_t ldx, uint8_t *q, int64_t ldq, float *s,
-                                 hipStream_t stream)
+static puro_status_t quant_act_impl(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                    uint8_t *q, int64_t ldq, float *s, bool pow2, hipStream_t stream)
 {
     try {
         puro_status_t st = check_quant(x, xdt, rows, cols, ldx, q, ldq, cols, s);
@@ -65,15 +62,15 @@ puro_status_t puro_fp8_quant_act(const void *x, puro_dtype_t xdt, int64_t rows, 
         if (rows == 0 || cols == 0)
             return PURO_OK;
         return from_hip(puro::launch_quant_act(x, xdt == PURO_BF16, rows, cols, ldx, q, ldq, s,
-                                               stream));
+                                               pow2, stream));
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }
 }
 
-puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,
-                                    int64_t ldw, uint8_t *q, int64_t ldq, float *s,
-                                    hipStream_t stream)
+static puro_status_t quant_weight_impl(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,
+                                       int64_t ldw, uint8_t *q, int64_t ldq, float *s, bool pow2,
+                                       hipStream_t stream)
 {
     try {
         puro_status_t st = check_quant(w, wdt, rows, cols, ldw, q, ldq, cols, s);
@@ -82,15 +79,15 @@ puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t row
         if (rows == 0 || cols == 0)
             return PURO_OK;
         return from_hip(puro::launch_quant_weight(w, wdt == PURO_BF16, rows, cols, ldw, q, ldq, s,
-                                                  stream));
+                                                  pow2, stream));
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }
 }
 
-puro_status_t puro_fp8_quant_transpose(const void *x, puro_dtype_t xdt, int64_t tokens,
-                                       int64_t cols, int64_t ldx, int transpose_out, uint8_t *q,
-                                       int64_t ldq, float *s, hipStream_t stream)
+static puro_status_t quant_transpose_impl(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                          int64_t ldx, int transpose_out, uint8_t *q, int64_t ldq, float *s,
+                                          bool pow2, hipStream_t stream)
 {
     try {
         if (transpose_out != 0 && transpose_out != 1)
@@ -102,16 +99,16 @@ puro_status_t puro_fp8_quant_transpose(const void *x, puro_dtype_t xdt, int64_t 
         if (tokens == 0 || cols == 0)
             return PURO_OK;
         return from_hip(puro::launch_quant_transpose(x, xdt == PURO_BF16, tokens, cols, ldx,
-                                                     transpose_out == 1, q, ldq, s, stream));
+                                                     transpose_out == 1, q, ldq, s, pow2, stream));
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }
 }
 
-puro_status_t puro_fp8_quant_dual(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
-                                  int64_t ldx, uint8_t *q_row, int64_t ldq_row, float *s_row,
-                                  int transpose_out, uint8_t *q_tok, int64_t ldq_tok, float *s_tok,
-                                  hipStream_t stream)
+static puro_status_t quant_dual_impl(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                     int64_t ldx, uint8_t *q_row, int64_t ldq_row, float *s_row,
+                                     int transpose_out, uint8_t *q_tok, int64_t ldq_tok, float *s_tok,
+                                     bool pow2, hipStream_t stream)
 {
     try {
         if (transpose_out != 0 && transpose_out != 1)
@@ -127,10 +124,67 @@ puro_status_t puro_fp8_quant_dual(const void *x, puro_dtype_t xdt, int64_t token
             return PURO_OK;
         return from_hip(puro::launch_quant_dual(x, xdt == PURO_BF16, tokens, cols, ldx, q_row,
                                                 ldq_row, s_row, transpose_out == 1, q_tok, ldq_tok,
-                                                s_tok, stream));
+                                                s_tok, pow2, stream));
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }
+}
+
+extern "C" {
+
+puro_status_t puro_fp8_quant_act(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t *q, int64_t ldq, float *s, hipStream_t stream)
+{
+    return quant_act_impl(x, xdt, rows, cols, ldx, q, ldq, s, false, stream);
+}
+
+puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols, int64_t ldw,
+                                    uint8_t *q, int64_t ldq, float *s, hipStream_t stream)
+{
+    return quant_weight_impl(w, wdt, rows, cols, ldw, q, ldq, s, false, stream);
+}
+
+puro_status_t puro_fp8_quant_transpose(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                       int64_t ldx, int transpose_out, uint8_t *q, int64_t ldq, float *s,
+                                       hipStream_t stream)
+{
+    return quant_transpose_impl(x, xdt, tokens, cols, ldx, transpose_out, q, ldq, s, false, stream);
+}
+
+puro_status_t puro_fp8_quant_dual(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols, int64_t ldx,
+                                  uint8_t *q_row, int64_t ldq_row, float *s_row, int transpose_out,
+                                  uint8_t *q_tok, int64_t ldq_tok, float *s_tok, hipStream_t stream)
+{
+    return quant_dual_impl(x, xdt, tokens, cols, ldx, q_row, ldq_row, s_row, transpose_out, q_tok, ldq_tok,
+                           s_tok, false, stream);
+}
+
+puro_status_t puro_fp8_quant_act_pow2(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                      uint8_t *q, int64_t ldq, float *s, hipStream_t stream)
+{
+    return quant_act_impl(x, xdt, rows, cols, ldx, q, ldq, s, true, stream);
+}
+
+puro_status_t puro_fp8_quant_weight_pow2(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,
+                                         int64_t ldw, uint8_t *q, int64_t ldq, float *s, hipStream_t stream)
+{
+    return quant_weight_impl(w, wdt, rows, cols, ldw, q, ldq, s, true, stream);
+}
+
+puro_status_t puro_fp8_quant_transpose_pow2(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                            int64_t ldx, int transpose_out, uint8_t *q, int64_t ldq, float *s,
+                                            hipStream_t stream)
+{
+    return quant_transpose_impl(x, xdt, tokens, cols, ldx, transpose_out, q, ldq, s, true, stream);
+}
+
+puro_status_t puro_fp8_quant_dual_pow2(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                       int64_t ldx, uint8_t *q_row, int64_t ldq_row, float *s_row,
+                                       int transpose_out, uint8_t *q_tok, int64_t ldq_tok, float *s_tok,
+                                       hipStream_t stream)
+{
+    return quant_dual_impl(x, xdt, tokens, cols, ldx, q_row, ldq_row, s_row, transpose_out, q_tok, ldq_tok,
+                           s_tok, true, stream);
 }
 
 static puro_status_t check_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
@@ -214,6 +268,47 @@ puro_status_t puro_fp8_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t 
         if (M == 0 || N == 0)
             return PURO_OK;
         return from_hip(puro::launch_gemm(p, workspace, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+static bool mx_aligned(int64_t M, int64_t N, int64_t K)
+{
+    return M % 128 == 0 && N % 128 == 0 && K % 128 == 0 && K > 0;
+}
+
+size_t puro_fp8_gemm_mx_workspace_size(puro_layout_t layout, int64_t M, int64_t N, int64_t K, puro_bscale_t bgran)
+{
+    if (layout != PURO_NT && layout != PURO_NN && layout != PURO_TN)
+        return 0;
+    if (bgran != PURO_SCALE_1x128 && bgran != PURO_SCALE_128x128)
+        return 0;
+    if (bad_extent(M) || bad_extent(N) || bad_extent(K) || !mx_aligned(M, N, K))
+        return 0;
+    puro::GemmProblem p = make_problem(layout, M, N, K, nullptr, 0, nullptr, nullptr, 0, nullptr, bgran, nullptr,
+                                       PURO_F32, N);
+    return puro::gemm_mx_workspace_bytes(p);
+}
+
+puro_status_t puro_fp8_gemm_mx(puro_layout_t layout, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                               int64_t lda, const float *sA, const uint8_t *B, int64_t ldb, const float *sB,
+                               puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc, void *workspace,
+                               size_t ws_bytes, hipStream_t stream)
+{
+    try {
+        puro_status_t st = check_gemm(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
+        if (st != PURO_OK)
+            return st;
+        if (M == 0 || N == 0)
+            return PURO_OK;
+        if (!mx_aligned(M, N, K))
+            return PURO_ERR_SHAPE;
+        puro::GemmProblem p = make_problem(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
+        const size_t need = puro::gemm_mx_workspace_bytes(p);
+        if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
+            return PURO_ERR_WORKSPACE;
+        return from_hip(puro::launch_gemm_mx(p, workspace, stream));
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }

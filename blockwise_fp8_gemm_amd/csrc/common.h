@@ -59,6 +59,28 @@ __device__ __forceinline__ float quotient(const Divider &d, float x)
     return __builtin_copysignf(fmaf(e, d.r, y0), x);
 }
 
+// Power-of-two block scale: the smallest s = 2^k with 448 s >= amax, k kept
+// in [-127, 127] (the E8M0 range of the scaled matrix cores; a zero block gets
+// 2^-127).  With amax = m 2^e (m in [0.5, 1)), 448 2^(e-9) = 0.875 2^e, so k
+// is e - 9 or e - 8; 448 2^k = 1.75 2^(k+8) is built exactly from its bits.
+__device__ __forceinline__ float pow2_scale(float amax)
+{
+    int e = -300;
+    if (amax > 0.0f)
+        frexpf(amax, &e);
+    int k = e - 9 < -127 ? -127 : e - 9;
+    if (k <= 119 && amax > __uint_as_float(((uint32_t)(k + 135) << 23) | 0x600000u))
+        k++;
+    return __uint_as_float(k >= -126 ? (uint32_t)(k + 127) << 23 : 0x00400000u);
+}
+
+// Dequantisation scale of a block with largest magnitude amax: amax / 448
+// (IEEE binary32 division), or the power-of-two rule.
+__device__ __forceinline__ float block_scale(float amax, int pow2)
+{
+    return pow2 ? pow2_scale(amax) : amax / 448.0f;
+}
+
 // Quantise four values of a block with dequant scale d.s (> 0, or == 0 for a
 // zero block: codes +-0 by sign).
 __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d_, const Divider &d)

@@ -361,6 +361,14 @@ __device__ __forceinline__ v8i fast_frag_mn(const uint8_t *t, int col_base, int 
     return r;
 }
 
+// E8M0 encoding of a power-of-two scale 2^k, k in [-127, 127]: the biased
+// exponent k + 127, which is the FP32 exponent field (0 for 2^-127, whose FP32
+// encoding is subnormal with only the top mantissa bit set).
+__device__ __forceinline__ int e8m0(float s)
+{
+    return (int)((__float_as_uint(s) >> 23) & 0xFFu);
+}
+
 struct V8H4 {
     v8h c[4];
 };
@@ -419,8 +427,9 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n)
 // One workgroup's output tile: rows [m0, m0 + TM) x columns [n0, n0 + TN) of
 // problem p, over K blocks [kb_lo, kb_hi) numbered across its segments.  With
 // OUT_PARTIAL the FP32 result goes to ws[split][M][N] (row stride N) instead
-// of C.  MULTI: p may have more than one segment.
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, bool MULTI>
+// of C.  MULTI: p may have more than one segment.  MX: the scales are powers
+// of two and the scaled FP8 matrix cores apply them (see the MX variant).
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, bool MULTI, bool MX = false>
 __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t n0, int64_t kb_lo,
                                           int64_t kb_hi, int split, float *ws)
 {
@@ -553,72 +562,101 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
         const uint8_t *tb = lds[buf] + A_BYTES;
         const int wrow = wm * IT * 16, wcol = wn * JT * 16;
 
-        // B's scales: with 128x128 weight tiles the wave's JT * 16 columns lie in
-        // one tile, so one scale serves them all and sA * sB is formed once per
-        // row; with 1x128 blocks each lane's column has its own scale.
-        static_assert(!BGRAN || 128 % (JT * 16) == 0, "wave columns within one weight tile");
-        float sbv[JT];
+        if constexpr (MX) {
+            // Scaled matrix cores: the E8M0 exponent of each power-of-two block
+            // scale goes to the MFMA, which scales the block's partial by
+            // sA sB and adds it to the accumulator (no promotion step and no
+            // widening: the MFMA takes the E4M3 codes as they are).
+            static_assert(!BGRAN || 128 % (JT * 16) == 0, "wave columns within one weight tile");
+            int sbe[JT];
+            v8i bf[JT];
 #pragma unroll
-        for (int j = 0; j < JT; j++)
-            sbv[j] = BGRAN ? lds_sc[buf][TM + (wcol >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)];
+            for (int j = 0; j < JT; j++) {
+                sbe[j] = e8m0(BGRAN ? lds_sc[buf][TM + (wcol >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)]);
+                bf[j] = B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane) : fast_frag_mn<TN>(tb, wcol + j * 16, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < IT; i++) {
+                const v8i af = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
+                const int sae = e8m0(lds_sc[buf][wrow + i * 16 + (lane & 15)]);
+#pragma unroll
+                for (int j = 0; j < JT; j++) {
+                    v4f c = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], c, 0, 0, 0, sae, 0, sbe[j]);
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[i][j][r] = c[r];
+                }
+            }
+        } else {
 
-        V8H4 bh[JT];
+            // B's scales: with 128x128 weight tiles the wave's JT * 16 columns lie in
+            // one tile, so one scale serves them all and sA * sB is formed once per
+            // row; with 1x128 blocks each lane's column has its own scale.
+            static_assert(!BGRAN || 128 % (JT * 16) == 0, "wave columns within one weight tile");
+            float sbv[JT];
 #pragma unroll
-        for (int j = 0; j < JT; j++)
-            bh[j] = widen32(B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane)
-                                   : fast_frag_mn<TN>(tb, wcol + j * 16, lane));
+            for (int j = 0; j < JT; j++)
+                sbv[j] = BGRAN ? lds_sc[buf][TM + (wcol >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)];
 
-        // A is widened one K sub-step (8 values per lane) at a time, right
-        // before its MFMAs, and the next row block's fragment is read as soon
-        // as the last sub-step of this one is widened; each sub-step runs over
-        // all JT tiles so that no MFMA waits on the one just issued.  Larger
-        // wave tiles (not INTERLEAVE) have no registers to spare for that:
-        // each row block is read and widened whole, and each tile's four
-        // MFMAs run back to back with one partial live.
-        constexpr bool INTERLEAVE = IT * JT <= 16;
-        v8i araw = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
+            V8H4 bh[JT];
 #pragma unroll
-        for (int i = 0; i < IT; i++) {
-            const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sc[buf][wrow + i * 16 + 4 * (lane >> 4)]);
-            const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
-            float sab[4];
+            for (int j = 0; j < JT; j++)
+                bh[j] = widen32(B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane)
+                                       : fast_frag_mn<TN>(tb, wcol + j * 16, lane));
+
+            // A is widened one K sub-step (8 values per lane) at a time, right
+            // before its MFMAs, and the next row block's fragment is read as soon
+            // as the last sub-step of this one is widened; each sub-step runs over
+            // all JT tiles so that no MFMA waits on the one just issued.  Larger
+            // wave tiles (not INTERLEAVE) have no registers to spare for that:
+            // each row block is read and widened whole, and each tile's four
+            // MFMAs run back to back with one partial live.
+            constexpr bool INTERLEAVE = IT * JT <= 16;
+            v8i araw = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-                sab[r] = sa[r] * sbv[0];
-            auto scale = [&](int j, int r) { return BGRAN ? sab[r] : sa[r] * sbv[j]; };
-            if (INTERLEAVE) {
-                v4f P[JT];
+            for (int i = 0; i < IT; i++) {
+                const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sc[buf][wrow + i * 16 + 4 * (lane >> 4)]);
+                const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+                float sab[4];
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const v8h aq = widen8(araw, q);
-                    if (q == 3 && i + 1 < IT)
-                        araw = A_KMAJ ? fast_frag_k(ta, wrow + (i + 1) * 16, lane)
-                                      : fast_frag_mn<TM>(ta, wrow + (i + 1) * 16, lane);
+                for (int r = 0; r < 4; r++)
+                    sab[r] = sa[r] * sbv[0];
+                auto scale = [&](int j, int r) { return BGRAN ? sab[r] : sa[r] * sbv[j]; };
+                if (INTERLEAVE) {
+                    v4f P[JT];
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const v8h aq = widen8(araw, q);
+                        if (q == 3 && i + 1 < IT)
+                            araw = A_KMAJ ? fast_frag_k(ta, wrow + (i + 1) * 16, lane)
+                                          : fast_frag_mn<TM>(ta, wrow + (i + 1) * 16, lane);
+#pragma unroll
+                        for (int j = 0; j < JT; j++) {
+                            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                            P[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bh[j].c[q], q ? P[j] : zero, 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < JT; j++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            acc[i][j][r] = fmaf(scale(j, r), P[j][r], acc[i][j][r]);
+                } else {
+                    if (i > 0)
+                        araw = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
+                    const V8H4 ah = widen32(araw);
 #pragma unroll
                     for (int j = 0; j < JT; j++) {
                         const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                        P[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bh[j].c[q], q ? P[j] : zero, 0, 0, 0);
+                        v4f P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[0], bh[j].c[0], zero, 0, 0, 0);
+#pragma unroll
+                        for (int q = 1; q < 4; q++)
+                            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[q], bh[j].c[q], P, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            acc[i][j][r] = fmaf(scale(j, r), P[r], acc[i][j][r]);
                     }
-                }
-#pragma unroll
-                for (int j = 0; j < JT; j++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        acc[i][j][r] = fmaf(scale(j, r), P[j][r], acc[i][j][r]);
-            } else {
-                if (i > 0)
-                    araw = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
-                const V8H4 ah = widen32(araw);
-#pragma unroll
-                for (int j = 0; j < JT; j++) {
-                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    v4f P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[0], bh[j].c[0], zero, 0, 0, 0);
-#pragma unroll
-                    for (int q = 1; q < 4; q++)
-                        P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[q], bh[j].c[q], P, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        acc[i][j][r] = fmaf(scale(j, r), P[r], acc[i][j][r]);
                 }
             }
         }
@@ -721,7 +759,7 @@ __device__ __forceinline__ GemmArgs load_args(KernargGemm src)
     return a;
 }
 
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL>
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, bool MX = false>
 __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs args, int tiles_m, int tiles_n,
                                                                  int splits, float *ws)
 {
@@ -735,7 +773,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs arg
     // split K only for single-segment products
     const int64_t KB = p.seg[0].KB;
     const int64_t kb_lo = KB * split / splits, kb_hi = KB * (split + 1) / splits;
-    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, OUT_PARTIAL, false>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN,
+    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, OUT_PARTIAL, false, MX>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN,
                                                              kb_lo, kb_hi, split, ws);
 }
 
@@ -820,7 +858,7 @@ constexpr int kComputeUnits = 256;
 // evenly over the CUs, so the busiest CU sets the time.  Splitting K adds
 // the partial sums, (splits + 1) M N 4 bytes moved at about 4 TB/s, and the
 // reduction launch.
-FastPlan fast_plan(int64_t M, int64_t N, int64_t K)
+FastPlan fast_plan(int64_t M, int64_t N, int64_t K, bool mx = false)
 {
     FastPlan best = {false, CFG_Q, 1};
     if (K <= 0 || K % 128 || M % CfgQ::TM || N % CfgQ::TN)
@@ -828,6 +866,8 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K)
     const int64_t KB = K / 128;
     double best_us = 1e300;
     for (int cfg : {CFG_L, CFG_Q}) {
+        if (mx && cfg != CFG_Q)   // the scaled-matrix-core variant is built for 128 x 128 tiles only
+            continue;
         const int TM = cfg == CFG_L ? CfgL::TM : CfgQ::TM, TN = cfg == CFG_L ? CfgL::TN : CfgQ::TN;
         if (M % TM || N % TN)
             continue;
@@ -839,6 +879,8 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K)
             const int64_t per_cu = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
             double us = cfg == CFG_L ? (double)per_cu * steps * 4.4 + 5.0
                                      : (double)(per_cu / 2) * steps * 2.3 + (double)(per_cu % 2) * steps * 1.8;
+            if (mx)   // no widening or promotion: about half the step time
+                us *= 0.5;
             if (sp > 1)
                 us += (double)(sp + 1) * (double)M * (double)N * 4.0 / 4e6 + 5.0;
             if (us < best_us) {
@@ -850,17 +892,17 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K)
     return best;
 }
 
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool MX = false>
 hipError_t launch_fast_cfg(const GemmArgs &a, int splits, float *ws, hipStream_t st)
 {
     const int tiles_m = (int)(a.M / Cfg::TM), tiles_n = (int)(a.N / Cfg::TN);
     const dim3 grid((unsigned)(tiles_m * tiles_n * splits));
     if (splits == 1) {
-        hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, false>), grid, dim3(Cfg::THREADS), 0,
+        hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, false, MX>), grid, dim3(Cfg::THREADS), 0,
                            st, a, tiles_m, tiles_n, 1, (float *)nullptr);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, true>), grid, dim3(Cfg::THREADS), 0, st,
+    hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, true, MX>), grid, dim3(Cfg::THREADS), 0, st,
                        a, tiles_m, tiles_n, splits, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -888,6 +930,23 @@ hipError_t launch_one(const GemmArgs &a, float *ws, hipStream_t st)
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
     hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+template <int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_mx_t(const GemmArgs &a, float *ws, hipStream_t st)
+{
+    const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K, true);
+    if (!plan.ok)
+        return hipErrorInvalidValue;   // the API layer admits aligned shapes only
+    return launch_fast_cfg<CfgQ, LAYOUT, BGRAN, CBF16, true>(a, plan.splits, ws, st);
+}
+
+template <int LAYOUT>
+hipError_t launch_mx_layout(const GemmProblem &p, const GemmArgs &a, float *ws, hipStream_t st)
+{
+    if (p.bgran)
+        return p.c_bf16 ? launch_mx_t<LAYOUT, 1, true>(a, ws, st) : launch_mx_t<LAYOUT, 1, false>(a, ws, st);
+    return p.c_bf16 ? launch_mx_t<LAYOUT, 0, true>(a, ws, st) : launch_mx_t<LAYOUT, 0, false>(a, ws, st);
 }
 
 template <int LAYOUT>
@@ -1047,6 +1106,27 @@ hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st)
     case 0: return launch_layout<0>(p, a, ws, st);
     case 1: return launch_layout<1>(p, a, ws, st);
     default: return launch_layout<2>(p, a, ws, st);
+    }
+}
+
+size_t gemm_mx_workspace_bytes(const GemmProblem &p)
+{
+    const FastPlan plan = fast_plan(p.M, p.N, p.seg[0].K, true);
+    if (!plan.ok || plan.splits == 1)
+        return 0;
+    return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+}
+
+hipError_t launch_gemm_mx(const GemmProblem &p, void *workspace, hipStream_t st)
+{
+    if (p.M == 0 || p.N == 0)
+        return hipSuccess;
+    const GemmArgs a = make_args(p);
+    float *ws = reinterpret_cast<float *>(workspace);
+    switch (p.layout) {
+    case 0: return launch_mx_layout<0>(p, a, ws, st);
+    case 1: return launch_mx_layout<1>(p, a, ws, st);
+    default: return launch_mx_layout<2>(p, a, ws, st);
     }
 }
 

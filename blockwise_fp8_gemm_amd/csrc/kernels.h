@@ -8,16 +8,18 @@
 
 namespace puro {
 
+// pow2: power-of-two block scales (the scaled matrix cores' E8M0 variant)
+// instead of amax / 448.
 hipError_t launch_quant_act(const void *x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
-                            uint8_t *q, int64_t ldq, float *s, hipStream_t st);
+                            uint8_t *q, int64_t ldq, float *s, bool pow2, hipStream_t st);
 hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t cols, int64_t ldw,
-                               uint8_t *q, int64_t ldq, float *s, hipStream_t st);
+                               uint8_t *q, int64_t ldq, float *s, bool pow2, hipStream_t st);
 hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int64_t cols,
                                   int64_t ldx, bool transpose_out, uint8_t *q, int64_t ldq,
-                                  float *s, hipStream_t st);
+                                  float *s, bool pow2, hipStream_t st);
 hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t cols, int64_t ldx,
                              uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
-                             int64_t ldqt, float *st, hipStream_t stream);
+                             int64_t ldqt, float *st, bool pow2, hipStream_t stream);
 
 constexpr int kGemmMaxSeg = 4;
 
@@ -50,6 +52,9 @@ struct GemmProblem {
 // grouped launcher's).
 size_t gemm_workspace_bytes(const GemmProblem &p);
 hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st);
+// Scaled-matrix-core variant: power-of-two scales, M, N, K multiples of 128.
+size_t gemm_mx_workspace_bytes(const GemmProblem &p);
+hipError_t launch_gemm_mx(const GemmProblem &p, void *workspace, hipStream_t st);
 // Independent problems sharing layout, B-scale granularity and output dtype;
 // needs no workspace.
 hipError_t launch_gemm_group(const GemmProblem *probs, int count, hipStream_t st);

@@ -2,6 +2,8 @@
 //
 // Each block of values x_i gets one FP32 dequantisation scale
 //   s = fl32(amax / 448),  q_i = E4M3_RNE(fl32(x_i / s)),
+// or, with pow2, s = the smallest power of two with 448 s >= amax (the scaled
+// matrix cores' E8M0 block scales),
 // with s == 0 (all-zero block, or amax/448 underflowing) stored as 0 and the
 // codes set to +-0 by sign.  Blocks are 1x128 along rows (activations and
 // gradients), 128x128 tiles (weights), or 128 consecutive tokens of one
@@ -30,7 +32,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void quant_act_kernel(const T *__restrict__ x, int64_t rows,
                                                         int64_t cols, int64_t ldx,
                                                         uint8_t *__restrict__ q, int64_t ldq,
-                                                        float *__restrict__ s, int64_t nb)
+                                                        float *__restrict__ s, int64_t nb, int pow2)
 {
     const int64_t runs = (nb + BPG - 1) / BPG;
     const int64_t grp = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const T *__restrict__ x,
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1)
             amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-        const float sc = amax / 448.0f;
+        const float sc = block_scale(amax, pow2);
         const Divider dv = make_divider(sc);
         const uint32_t lo = quant4(v[u][0], v[u][1], v[u][2], v[u][3], dv);
         const uint32_t hi = quant4(v[u][4], v[u][5], v[u][6], v[u][7], dv);
@@ -94,7 +96,7 @@ template <typename T>
 __global__ __launch_bounds__(1024) void quant_weight_kernel(const T *__restrict__ w, int64_t rows,
                                                             int64_t cols, int64_t ldw,
                                                             uint8_t *__restrict__ q, int64_t ldq,
-                                                            float *__restrict__ s, int64_t cb)
+                                                            float *__restrict__ s, int64_t cb, int pow2)
 {
     __shared__ float red[16];
     const int t = threadIdx.x;
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(1024) void quant_weight_kernel(const T *__restrict_
 #pragma unroll
     for (int i = 1; i < 16; i++)
         amax = fmaxf(amax, red[i]);
-    const float sc = amax / 448.0f;
+    const float sc = block_scale(amax, pow2);
     const Divider dv = make_divider(sc);
 
 #pragma unroll
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
                                                               int64_t tokens, int64_t cols,
                                                               int64_t ldx, uint8_t *__restrict__ q,
                                                               int64_t ldq, float *__restrict__ s,
-                                                              int64_t ntb)
+                                                              int64_t ntb, int pow2)
 {
     __shared__ float red[4][64];
     __shared__ float scl[64];
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
     __syncthreads();
     if (t < 64) {
         const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
-        const float sc = amax / 448.0f;
+        const float sc = block_scale(amax, pow2);
         scl[t] = sc;
         const int64_t c = col0 + t;
         if (c < cols) {
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
                                                          uint8_t *__restrict__ qr, int64_t ldqr,
                                                          float *__restrict__ sr, int64_t nbr,
                                                          uint8_t *__restrict__ qt, int64_t ldqt,
-                                                         float *__restrict__ st, int64_t ntb)
+                                                         float *__restrict__ st, int64_t ntb, int pow2)
 {
     __shared__ float red[4][128];
     __shared__ float scl[128];
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
     __syncthreads();
     if (t < 128) {
         const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
-        const float sc = amax / 448.0f;
+        const float sc = block_scale(amax, pow2);
         scl[t] = sc;
         const int64_t c = col0 + t;
         if (c < cols) {
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1)
             a = fmaxf(a, __shfl_xor(a, off, 16));
-        const float sc = a / 448.0f;
+        const float sc = block_scale(a, pow2);
         const Divider dv = make_divider(sc);
         const uint32_t lo = quant4(v[i][0], v[i][1], v[i][2], v[i][3], dv);
         const uint32_t hi = quant4(v[i][4], v[i][5], v[i][6], v[i][7], dv);
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
 // ---------------------------------------------------------------------------
 
 hipError_t launch_quant_act(const void *x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
-                            uint8_t *q, int64_t ldq, float *s, hipStream_t st)
+                            uint8_t *q, int64_t ldq, float *s, bool pow2, hipStream_t st)
 {
     const int64_t nb = (cols + 127) / 128;
     const int64_t groups = rows * ((nb + BPG - 1) / BPG);
@@ -444,15 +446,15 @@ hipError_t launch_quant_act(const void *x, bool bf16, int64_t rows, int64_t cols
     const dim3 grid((unsigned)((groups + 15) / 16));
     if (bf16)
         hipLaunchKernelGGL(quant_act_kernel<uint16_t>, grid, dim3(256), 0, st,
-                           (const uint16_t *)x, rows, cols, ldx, q, ldq, s, nb);
+                           (const uint16_t *)x, rows, cols, ldx, q, ldq, s, nb, (int)pow2);
     else
         hipLaunchKernelGGL(quant_act_kernel<float>, grid, dim3(256), 0, st, (const float *)x, rows,
-                           cols, ldx, q, ldq, s, nb);
+                           cols, ldx, q, ldq, s, nb, (int)pow2);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t cols, int64_t ldw,
-                               uint8_t *q, int64_t ldq, float *s, hipStream_t st)
+                               uint8_t *q, int64_t ldq, float *s, bool pow2, hipStream_t st)
 {
     const int64_t rb = (rows + 127) / 128, cb = (cols + 127) / 128;
     if (rb == 0 || cb == 0)
@@ -460,16 +462,16 @@ hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t c
     const dim3 grid((unsigned)cb, (unsigned)rb);
     if (bf16)
         hipLaunchKernelGGL(quant_weight_kernel<uint16_t>, grid, dim3(1024), 0, st,
-                           (const uint16_t *)w, rows, cols, ldw, q, ldq, s, cb);
+                           (const uint16_t *)w, rows, cols, ldw, q, ldq, s, cb, (int)pow2);
     else
         hipLaunchKernelGGL(quant_weight_kernel<float>, grid, dim3(1024), 0, st, (const float *)w,
-                           rows, cols, ldw, q, ldq, s, cb);
+                           rows, cols, ldw, q, ldq, s, cb, (int)pow2);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int64_t cols,
                                   int64_t ldx, bool transpose_out, uint8_t *q, int64_t ldq,
-                                  float *s, hipStream_t st)
+                                  float *s, bool pow2, hipStream_t st)
 {
     const int64_t ntb = (tokens + 127) / 128, ncg = (cols + 63) / 64;
     if (ntb == 0 || ncg == 0)
@@ -478,24 +480,24 @@ hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int6
     if (bf16) {
         if (transpose_out)
             hipLaunchKernelGGL((quant_transpose_kernel<uint16_t, true>), grid, dim3(256), 0, st,
-                               (const uint16_t *)x, tokens, cols, ldx, q, ldq, s, ntb);
+                               (const uint16_t *)x, tokens, cols, ldx, q, ldq, s, ntb, (int)pow2);
         else
             hipLaunchKernelGGL((quant_transpose_kernel<uint16_t, false>), grid, dim3(256), 0, st,
-                               (const uint16_t *)x, tokens, cols, ldx, q, ldq, s, ntb);
+                               (const uint16_t *)x, tokens, cols, ldx, q, ldq, s, ntb, (int)pow2);
     } else {
         if (transpose_out)
             hipLaunchKernelGGL((quant_transpose_kernel<float, true>), grid, dim3(256), 0, st,
-                               (const float *)x, tokens, cols, ldx, q, ldq, s, ntb);
+                               (const float *)x, tokens, cols, ldx, q, ldq, s, ntb, (int)pow2);
         else
             hipLaunchKernelGGL((quant_transpose_kernel<float, false>), grid, dim3(256), 0, st,
-                               (const float *)x, tokens, cols, ldx, q, ldq, s, ntb);
+                               (const float *)x, tokens, cols, ldx, q, ldq, s, ntb, (int)pow2);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t cols, int64_t ldx,
                              uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
-                             int64_t ldqt, float *st, hipStream_t stream)
+                             int64_t ldqt, float *st, bool pow2, hipStream_t stream)
 {
     const int64_t ntb = (tokens + 127) / 128, ncb = (cols + 127) / 128;
     if (ntb == 0 || ncb == 0)
@@ -503,7 +505,7 @@ hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t c
     const dim3 grid((unsigned)ncb, (unsigned)ntb);
 #define PURO_DUAL(T, TR)                                                                            \
     hipLaunchKernelGGL((quant_dual_kernel<T, TR>), grid, dim3(256), 0, stream, (const T *)x, tokens, \
-                       cols, ldx, qr, ldqr, sr, ncb, qt, ldqt, st, ntb)
+                       cols, ldx, qr, ldqr, sr, ncb, qt, ldqt, st, ntb, (int)pow2)
     if (bf16) {
         if (transpose_out)
             PURO_DUAL(uint16_t, true);

@@ -216,6 +216,55 @@ typedef struct {
 puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
                                     const puro_gemm_desc_t *problems, int count, hipStream_t stream);
 
+/*
+ * Power-of-two scale variant (for the scaled FP8 matrix cores).
+ *
+ * Not the recipe: the pages give no scale rule, and the recipe's reading
+ * (s = amax / 448) is what the calls above implement.  gfx950's scaled MFMA
+ * takes one E8M0 scale (a power of two) per 32 K values of each row of A and
+ * column of B, applies it inside the matrix core and accumulates across K
+ * blocks without a separate promotion step, on E4M3 codes as they are.  With
+ * power-of-two block scales the same 1x128 / 128x128 blocks map onto it.
+ *
+ * The _pow2 quantisers take the arguments of their counterparts above and
+ * write the same layouts; per block the scale is the smallest power of two
+ * s = 2^k with 448 s >= amax (k limited to [-127, 127]; a zero block gets
+ * 2^-127) and q = E4M3(x / s), where x / s is exact.
+ */
+puro_status_t puro_fp8_quant_act_pow2(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                      uint8_t *q, int64_t ldq, float *s, hipStream_t stream);
+puro_status_t puro_fp8_quant_weight_pow2(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,
+                                         int64_t ldw, uint8_t *q, int64_t ldq, float *s, hipStream_t stream);
+puro_status_t puro_fp8_quant_transpose_pow2(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                            int64_t ldx, int transpose_out, uint8_t *q, int64_t ldq, float *s,
+                                            hipStream_t stream);
+puro_status_t puro_fp8_quant_dual_pow2(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
+                                       int64_t ldx, uint8_t *q_row, int64_t ldq_row, float *s_row,
+                                       int transpose_out, uint8_t *q_tok, int64_t ldq_tok, float *s_tok,
+                                       hipStream_t stream);
+
+/*
+ * GEMM on the scaled FP8 matrix cores: arguments, storage and result
+ * definition of puro_fp8_gemm, with two differences.
+ *   - sA and sB must hold powers of two in [2^-127, 2^127] (as written by the
+ *     _pow2 quantisers): only their exponents reach the matrix cores, so any
+ *     other value gives wrong results.
+ *   - M, N and K must be multiples of 128 (else PURO_ERR_SHAPE; empty
+ *     products are allowed and do nothing).
+ * Precision: the FP8 matrix cores add each run of 8 consecutive products in
+ * fixed point, dropping bits more than about 13 binary places below the
+ * run's largest product (measured on gfx950), so the result is not FP32-exact
+ * per block: the relative error is of order 1e-5 to 1e-4, against 2e-6 for
+ * puro_fp8_gemm.  workspace as for puro_fp8_gemm, sized by
+ * puro_fp8_gemm_mx_workspace_size (0 for invalid arguments).
+ */
+size_t puro_fp8_gemm_mx_workspace_size(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                                       puro_bscale_t bgran);
+puro_status_t puro_fp8_gemm_mx(puro_layout_t layout, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                               int64_t lda, const float *sA, const uint8_t *B, int64_t ldb, const float *sB,
+                               puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc, void *workspace,
+                               size_t ws_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *puro_status_string(puro_status_t status);
 

@@ -31,7 +31,9 @@ def test_header_declares_the_calls():
     names = _declared()
     for n in ("puro_fp8_quant_act", "puro_fp8_quant_weight", "puro_fp8_quant_transpose",
               "puro_fp8_gemm", "puro_fp8_gemm_workspace_size", "puro_fp8_gemm_grouped",
-              "puro_fp8_quant_dual", "puro_status_string",
+              "puro_fp8_quant_dual", "puro_fp8_quant_act_pow2", "puro_fp8_quant_weight_pow2",
+              "puro_fp8_quant_transpose_pow2", "puro_fp8_quant_dual_pow2", "puro_fp8_gemm_mx",
+              "puro_fp8_gemm_mx_workspace_size", "puro_status_string",
               "puro_fp8_version"):
         assert n in names
 
@@ -65,7 +67,15 @@ def _qt(x=P, dt=1, tokens=256, cols=64, ldx=64, t=1, q=P, ldq=256, s=P):
     return pf.lib().puro_fp8_quant_transpose(x, dt, tokens, cols, ldx, t, q, ldq, s, None)
 
 
-@pytest.mark.parametrize("fn", [_qa, _qw])
+def _qa2(x=P, dt=1, rows=4, cols=128, ldx=128, q=P, ldq=128, s=P):
+    return pf.lib().puro_fp8_quant_act_pow2(x, dt, rows, cols, ldx, q, ldq, s, None)
+
+
+def _qw2(x=P, dt=0, rows=128, cols=128, ldx=128, q=P, ldq=128, s=P):
+    return pf.lib().puro_fp8_quant_weight_pow2(x, dt, rows, cols, ldx, q, ldq, s, None)
+
+
+@pytest.mark.parametrize("fn", [_qa, _qw, _qa2, _qw2])
 def test_quant_validation(fn):
     assert fn(dt=2) == ENUM
     assert fn(dt=-1) == ENUM
@@ -187,3 +197,36 @@ def test_workspace_size_is_defined_for_every_layout():
         for bg in ("1x128", "128x128"):
             assert pf.puro_fp8_gemm_workspace_size(layout, 8192, 2048, 8192, bg) >= 0
     assert pf.lib().puro_fp8_gemm_workspace_size(9, 128, 128, 128, 0) == 0
+
+
+def test_pow2_transpose_and_dual_validation():
+    L = pf.lib()
+    assert L.puro_fp8_quant_transpose_pow2(P, 1, 256, 64, 64, 2, P, 256, P, None) == ENUM
+    assert L.puro_fp8_quant_transpose_pow2(P, 1, 256, 64, 64, 1, P, 128, P, None) == SHAPE
+    assert L.puro_fp8_quant_transpose_pow2(NUL, 1, 0, 64, 64, 1, NUL, 0, NUL, None) == OK
+    assert L.puro_fp8_quant_dual_pow2(P, 1, 256, 128, 128, P, 128, P, 3, P, 256, P, None) == ENUM
+    assert L.puro_fp8_quant_dual_pow2(P, 1, 256, 128, 128, P, 128, P, 1, NUL, 256, P, None) == NULL
+    assert L.puro_fp8_quant_dual_pow2(NUL, 1, 0, 128, 128, NUL, 128, NUL, 1, NUL, 0, NUL, None) == OK
+
+
+def _gmx(layout=0, M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, bg=1, C=P, cdt=1, ldc=256,
+         ws=NUL, wsb=0):
+    return pf.lib().puro_fp8_gemm_mx(layout, M, N, K, A, lda, sA, B, ldb, sB, bg, C, cdt, ldc, ws, wsb, None)
+
+
+def test_gemm_mx_validation():
+    assert _gmx(layout=3) == ENUM
+    assert _gmx(cdt=5) == ENUM
+    assert _gmx(M=-1) == SHAPE
+    assert _gmx(ldc=128) == SHAPE
+    assert _gmx(A=NUL) == NULL
+    assert _gmx(C=P_ODD) == ALIGN
+    # extents must be multiples of 128
+    assert _gmx(M=200) == SHAPE
+    assert _gmx(N=136, ldb=256, ldc=256) == SHAPE
+    assert _gmx(K=192) == SHAPE
+    assert _gmx(K=0, A=NUL, sA=NUL, B=NUL, sB=NUL) == SHAPE
+    # empty outputs: nothing enqueued
+    assert _gmx(M=0, A=NUL, sA=NUL, C=NUL) == OK
+    assert pf.puro_fp8_gemm_mx_workspace_size("NT", 200, 256, 256, "1x128") == 0
+    assert pf.puro_fp8_gemm_mx_workspace_size("NT", 256, 256, 8192, "1x128") >= 0
