@@ -283,7 +283,9 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
 // of the 8 consecutive tokens 8*(t/16) .. +7 (64 values in registers).
 // Row amax: cross-lane max over the 16 lanes with equal t/16.  Column amax:
 // per-thread max over its 8 tokens, cross-lane max over lanes with equal
-// t%16, then across the 4 waves through LDS.
+// t%16, then across the 4 waves through LDS.  This general form serves FP32
+// input, the untransposed token-block copy and the ragged edge tiles of the
+// packed BF16 kernel below; (bx0, by0) offsets the tile grid for the latter.
 // ---------------------------------------------------------------------------
 template <typename T, bool TRANSPOSE_OUT>
 __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x, int64_t tokens,
@@ -291,7 +293,8 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
                                                          uint8_t *__restrict__ qr, int64_t ldqr,
                                                          float *__restrict__ sr, int64_t nbr,
                                                          uint8_t *__restrict__ qt, int64_t ldqt,
-                                                         float *__restrict__ st, int64_t ntb, int pow2)
+                                                         float *__restrict__ st, int64_t ntb, int pow2,
+                                                         int bx0, int by0)
 {
     __shared__ float red[4][128];
     __shared__ float scl[128];
@@ -299,8 +302,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int cc = t & 15, rq = t >> 4;
-    const int64_t tok0 = (int64_t)blockIdx.y * 128;
-    const int64_t col0 = (int64_t)blockIdx.x * 128;
+    const unsigned bx = blockIdx.x + bx0, by = blockIdx.y + by0;
+    const int64_t tok0 = (int64_t)by * 128;
+    const int64_t col0 = (int64_t)bx * 128;
     const int64_t c0 = col0 + cc * 8;
     const bool full = (tok0 + 128 <= tokens) && (col0 + 128 <= cols);
 
@@ -343,9 +347,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
         const int64_t c = col0 + t;
         if (c < cols) {
             if (TRANSPOSE_OUT)
-                st[c * ntb + blockIdx.y] = sc;
+                st[c * ntb + by] = sc;
             else
-                st[(int64_t)blockIdx.y * cols + c] = sc;
+                st[(int64_t)by * cols + c] = sc;
         }
     }
 
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
                     q[c0 + j] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFF);
         }
         if (cc == 0 && tk < tokens)
-            sr[tk * nbr + blockIdx.x] = sc;
+            sr[tk * nbr + bx] = sc;
     }
     __syncthreads();
 
@@ -431,6 +435,219 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
                         q[c0 + j] = (uint8_t)b[j];
             }
         }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Dual quantiser, BF16 input, token-blocked copy transposed.  Same tile and
+// thread mapping as quant_dual_kernel, but the 64 values stay packed as BF16
+// pairs (32 registers), block maxima are taken on the magnitude bits as
+// 16-bit integers (finite inputs: the order of |x| is the order of its bits),
+// two at a time, and each block's scale and reciprocal are computed once and
+// shared through LDS.
+// ---------------------------------------------------------------------------
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pmax16(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+__device__ __forceinline__ uint32_t pshl1(uint32_t a)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) << (unsigned short)1);
+}
+
+// Max over each row of 16 lanes (DPP row rotates; every lane ends with it).
+__device__ __forceinline__ uint32_t rowmax16(uint32_t v)
+{
+    v = pmax16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+    v = pmax16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+    v = pmax16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));
+    v = pmax16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));
+    return v;
+}
+
+// Scale and reciprocal of a block; r = 0 for a zero scale (codes +-0 by sign
+// through the fast path) and for scales below 2^-80 (divided exactly).
+struct ScaleRcp {
+    float s, r;
+};
+__device__ __forceinline__ ScaleRcp scale_rcp(uint32_t amax_bits, int pow2)
+{
+    ScaleRcp o;
+    o.s = block_scale(__uint_as_float(amax_bits), pow2);
+    // a power-of-two scale divides exactly through its reciprocal at any size
+    o.r = (pow2 || o.s >= 0x1p-80f) ? 1.0f / o.s : 0.0f;
+    return o;
+}
+__device__ __forceinline__ bool slow_div(float s, float r) { return r == 0.0f && s != 0.0f; }
+
+template <bool SLOW>
+__device__ __forceinline__ float qdiv(float x, float s, float r)
+{
+    if (SLOW && slow_div(s, r))
+        return x / s;
+    const float y0 = x * r;
+    const float e = fmaf(-y0, s, x);
+    return __builtin_copysignf(fmaf(e, r, y0), x);
+}
+
+template <bool SLOW>
+__device__ __forceinline__ uint32_t q4(float a, float b, float c, float d, float s, float r)
+{
+    return e4m3x4(qdiv<SLOW>(a, s, r), qdiv<SLOW>(b, s, r), qdiv<SLOW>(c, s, r), qdiv<SLOW>(d, s, r));
+}
+
+__device__ __forceinline__ float lo16f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi16f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Quantise this thread's 8 tokens x 8 columns both ways: row codes straight to
+// global memory, token-block codes into the LDS tile.
+template <bool SLOW>
+__device__ __forceinline__ void dual_bf16_quant(uint32_t (&raw)[8][4], const float2 *rsc,
+                                                const float *scl, const float *rcl,
+                                                uint32_t (*tile)[33], uint8_t *qr_t, int ldqr,
+                                                int rq, int cc)
+{
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float2 sr = rsc[8 * rq + i];
+        const uint32_t lo = e4m3x4(qdiv<SLOW>(lo16f(raw[i][0]), sr.x, sr.y), qdiv<SLOW>(hi16f(raw[i][0]), sr.x, sr.y),
+                                   qdiv<SLOW>(lo16f(raw[i][1]), sr.x, sr.y), qdiv<SLOW>(hi16f(raw[i][1]), sr.x, sr.y));
+        const uint32_t hi = e4m3x4(qdiv<SLOW>(lo16f(raw[i][2]), sr.x, sr.y), qdiv<SLOW>(hi16f(raw[i][2]), sr.x, sr.y),
+                                   qdiv<SLOW>(lo16f(raw[i][3]), sr.x, sr.y), qdiv<SLOW>(hi16f(raw[i][3]), sr.x, sr.y));
+        *reinterpret_cast<uint2 *>(qr_t + (8 * rq + i) * ldqr + cc * 8) = make_uint2(lo, hi);
+    }
+    // Keep the values packed between the two passes: without this the compiler
+    // holds the row pass's 64 unpacked floats for the column pass.
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int p = 0; p < 4; p++)
+            asm volatile("" : "+v"(raw[i][p]));
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const float s0 = scl[cc * 8 + 2 * p], r0 = rcl[cc * 8 + 2 * p];
+        const float s1 = scl[cc * 8 + 2 * p + 1], r1 = rcl[cc * 8 + 2 * p + 1];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            tile[cc * 8 + 2 * p][2 * rq + h] =
+                q4<SLOW>(lo16f(raw[4 * h][p]), lo16f(raw[4 * h + 1][p]), lo16f(raw[4 * h + 2][p]),
+                         lo16f(raw[4 * h + 3][p]), s0, r0);
+            tile[cc * 8 + 2 * p + 1][2 * rq + h] =
+                q4<SLOW>(hi16f(raw[4 * h][p]), hi16f(raw[4 * h + 1][p]), hi16f(raw[4 * h + 2][p]),
+                         hi16f(raw[4 * h + 3][p]), s1, r1);
+        }
+    }
+}
+
+__device__ __forceinline__ void dual_bf16_load(uint32_t (&raw)[8][4], const uint16_t *x_t, int ldx,
+                                               int rq, int cc)
+{
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(x_t + (8 * rq + i) * ldx + cc * 8);
+        raw[i][0] = a.x; raw[i][1] = a.y; raw[i][2] = a.z; raw[i][3] = a.w;
+    }
+}
+
+// Tiles holding a block whose scale is below 2^-80 (never in practice): reload
+// the values and divide those blocks exactly, outside the fast kernel body.
+__device__ __attribute__((noinline)) void dual_bf16_slow(const uint16_t *x_t, int ldx,
+                                                         const float2 *rsc, const float *scl,
+                                                         const float *rcl, uint32_t (*tile)[33],
+                                                         uint8_t *qr_t, int ldqr, int rq, int cc)
+{
+    uint32_t raw[8][4];
+    dual_bf16_load(raw, x_t, ldx, rq, cc);
+    dual_bf16_quant<true>(raw, rsc, scl, rcl, tile, qr_t, ldqr, rq, cc);
+}
+
+// Full 128 x 128 tiles only (the launcher sends ragged edge tiles to
+// quant_dual_kernel); offsets inside a tile fit 32 bits (checked by the launcher).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
+void quant_dual_bf16_kernel(const uint16_t *__restrict__ x, int ldx, uint8_t *__restrict__ qr,
+                            int ldqr, float *__restrict__ sr, int64_t nbr,
+                            uint8_t *__restrict__ qt, int ldqt, float *__restrict__ st,
+                            int64_t ntb, int pow2)
+{
+    __shared__ uint32_t red[4][64];           // [wave][column pair] packed column maxima
+    __shared__ float scl[128], rcl[128];       // column scales and reciprocals
+    __shared__ float2 rsc[128];                // row (token) scale and reciprocal
+    __shared__ uint32_t tile[128][32 + 1];     // [column][token/4] codes, odd stride
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int cc = t & 15, rq = t >> 4, l16 = t & 15;
+    const int64_t tok0 = (int64_t)blockIdx.y * 128;
+    const int64_t col0 = (int64_t)blockIdx.x * 128;
+    const uint16_t *x_t = x + tok0 * ldx + col0;
+
+    uint32_t raw[8][4];
+    dual_bf16_load(raw, x_t, ldx, rq, cc);
+    constexpr uint32_t MAG = 0x7FFF7FFFu;
+
+    // ---- column partial maxima over this thread's 8 tokens, then the wave's 4 rows
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        // magnitudes doubled (each half shifted left by one, dropping its sign)
+        uint32_t m = pshl1(raw[0][p]);
+#pragma unroll
+        for (int i = 1; i < 8; i++)
+            m = pmax16(m, pshl1(raw[i][p]));
+        m = pmax16(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+        m = pmax16(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+        if (lane < 16)
+            red[wave][cc * 4 + p] = m;
+    }
+
+    // ---- row maxima: tokens 2k, 2k+1 packed into one register, reduced over the 16 lanes
+    uint32_t rp[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t a = pmax16(pmax16(raw[2 * k][0] & MAG, raw[2 * k][1] & MAG),
+                                  pmax16(raw[2 * k][2] & MAG, raw[2 * k][3] & MAG));
+        const uint32_t b = pmax16(pmax16(raw[2 * k + 1][0] & MAG, raw[2 * k + 1][1] & MAG),
+                                  pmax16(raw[2 * k + 1][2] & MAG, raw[2 * k + 1][3] & MAG));
+        rp[k] = rowmax16(pmax16(__builtin_amdgcn_perm(b, a, 0x05040100u),
+                                __builtin_amdgcn_perm(b, a, 0x07060302u)));
+    }
+    // lane l16 < 8 of each row group owns token 8 rq + l16
+    bool slow;
+    {
+        const int i = l16 & 7;
+        const uint32_t pr = (i >> 1) == 0 ? rp[0] : (i >> 1) == 1 ? rp[1] : (i >> 1) == 2 ? rp[2] : rp[3];
+        const ScaleRcp o = scale_rcp((i & 1) ? (pr & 0xFFFF0000u) : (pr << 16), pow2);
+        slow = slow_div(o.s, o.r);
+        if (l16 < 8) {
+            rsc[8 * rq + i] = make_float2(o.s, o.r);
+            sr[(tok0 + 8 * rq + i) * nbr + blockIdx.x] = o.s;
+        }
+    }
+    __syncthreads();
+    if (t < 128) {
+        const uint32_t m = pmax16(pmax16(red[0][t >> 1], red[1][t >> 1]), pmax16(red[2][t >> 1], red[3][t >> 1]));
+        const ScaleRcp o = scale_rcp((t & 1) ? ((m >> 1) & 0x7FFF0000u) : ((m & 0xFFFFu) << 15), pow2);
+        scl[t] = o.s;
+        rcl[t] = o.r;
+        st[(col0 + t) * ntb + blockIdx.y] = o.s;
+        slow = slow || slow_div(o.s, o.r);
+    }
+    uint8_t *qr_t = qr + tok0 * ldqr + col0;
+    if (__syncthreads_or(slow))
+        dual_bf16_slow(x_t, ldx, rsc, scl, rcl, tile, qr_t, ldqr, rq, cc);
+    else
+        dual_bf16_quant<false>(raw, rsc, scl, rcl, tile, qr_t, ldqr, rq, cc);
+    __syncthreads();
+    uint8_t *qt_t = qt + col0 * ldqt + tok0;
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+        const int chunk = t + 256 * it;
+        const int row = chunk >> 3, seg = chunk & 7;
+        const uint32_t *src = &tile[row][seg * 4];
+        *reinterpret_cast<uint4 *>(qt_t + row * ldqt + seg * 16) = make_uint4(src[0], src[1], src[2], src[3]);
     }
 }
 
@@ -502,22 +719,47 @@ hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t c
     const int64_t ntb = (tokens + 127) / 128, ncb = (cols + 127) / 128;
     if (ntb == 0 || ncb == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)ncb, (unsigned)ntb);
+    // full tiles of BF16 input with a transposed token-block copy: packed kernel
+    // (in-tile offsets of at most 127 leading dimensions must fit 32 bits)
+    int64_t fb_x = 0, fb_y = 0;
+    const int64_t lim = ((int64_t)1 << 31) / 256;
+    if (bf16 && transpose_out && ldx < lim && ldqr < lim && ldqt < lim) {
+        fb_x = cols / 128;
+        fb_y = tokens / 128;
+        if (fb_x > 0 && fb_y > 0)
+            hipLaunchKernelGGL(quant_dual_bf16_kernel, dim3((unsigned)fb_x, (unsigned)fb_y), dim3(256), 0,
+                               stream, (const uint16_t *)x, (int)ldx, qr, (int)ldqr, sr, ncb, qt, (int)ldqt,
+                               st, ntb, (int)pow2);
+        else
+            fb_x = fb_y = 0;
+    }
+    // the rest: tiles right of the full columns (all token tiles), then the tiles
+    // below the full rows (full columns only)
+    auto rest = [&](dim3 grid, int bx0, int by0) {
 #define PURO_DUAL(T, TR)                                                                            \
     hipLaunchKernelGGL((quant_dual_kernel<T, TR>), grid, dim3(256), 0, stream, (const T *)x, tokens, \
-                       cols, ldx, qr, ldqr, sr, ncb, qt, ldqt, st, ntb, (int)pow2)
-    if (bf16) {
-        if (transpose_out)
-            PURO_DUAL(uint16_t, true);
-        else
-            PURO_DUAL(uint16_t, false);
-    } else {
-        if (transpose_out)
-            PURO_DUAL(float, true);
-        else
-            PURO_DUAL(float, false);
-    }
+                       cols, ldx, qr, ldqr, sr, ncb, qt, ldqt, st, ntb, (int)pow2, bx0, by0)
+        if (bf16) {
+            if (transpose_out)
+                PURO_DUAL(uint16_t, true);
+            else
+                PURO_DUAL(uint16_t, false);
+        } else {
+            if (transpose_out)
+                PURO_DUAL(float, true);
+            else
+                PURO_DUAL(float, false);
+        }
 #undef PURO_DUAL
+    };
+    if (fb_x == 0 || fb_y == 0) {
+        rest(dim3((unsigned)ncb, (unsigned)ntb), 0, 0);
+    } else {
+        if (ncb > fb_x)
+            rest(dim3((unsigned)(ncb - fb_x), (unsigned)ntb), (int)fb_x, 0);
+        if (ntb > fb_y)
+            rest(dim3((unsigned)fb_x, (unsigned)(ntb - fb_y)), 0, (int)fb_y);
+    }
     return hipGetLastError();
 }
 
