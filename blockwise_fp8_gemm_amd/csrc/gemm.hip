@@ -130,6 +130,7 @@ __device__ __forceinline__ v8i frag_mnmajor(const uint8_t *lds, int col_base, in
 }
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 // Bytes 8c .. 8c+7 of an E4M3 fragment as eight FP16 values (exact).
@@ -336,12 +337,11 @@ __device__ __forceinline__ v8i fast_frag_k(const uint8_t *t, int row_base, int l
 {
     const int row = row_base + (lane & 15);
     const int g = lane >> 4, f = (row >> 1) & 7;
-    const uint4 lo = *reinterpret_cast<const uint4 *>(t + row * 128 + (((2 * g) ^ f) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4 *>(t + row * 128 + (((2 * g + 1) ^ f) << 4));
-    v8i r;
-    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-    return r;
+    // whole 16-byte vector loads (not four dword loads merged later), which
+    // keeps each read's LDS object visible to the compiler
+    const v4i lo = *reinterpret_cast<const v4i *>(t + (row * 128 + (((2 * g) ^ f) << 4)));
+    const v4i hi = *reinterpret_cast<const v4i *>(t + (row * 128 + (((2 * g + 1) ^ f) << 4)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <int W>
@@ -353,7 +353,9 @@ __device__ __forceinline__ v8i fast_frag_mn(const uint8_t *t, int col_base, int 
 #pragma unroll
     for (int q = 0; q < 4; q++) {
         const int k = 32 * g + 8 * q + (i >> 1);
-        const uint8_t *a = t + k * W + ((seg ^ (k & 7)) << 4) + within;
+        // one offset added to the stage pointer (not a chain of pointer
+        // additions), which keeps the read's LDS object visible to the compiler
+        const uint8_t *a = t + (k * W + ((seg ^ (k & 7)) << 4) + within);
         const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)a);
         r[2 * q] = v[0];
         r[2 * q + 1] = v[1];
@@ -391,6 +393,11 @@ struct FastCfg {
     // direct copies each wave issues per K block: A and B tiles in 1 KB
     // pieces, plus one 4-byte-per-lane copy for the block's scales
     static constexpr int LOADS = TM / 8 / NW + TN / 8 / NW + 1;
+    // K loop unrolled by the two stages, so that each stage is addressed by a
+    // compile-time name: the compiler then sees that the copies into one stage
+    // do not touch the other and lets the copies overlap the reads.  Costs
+    // registers, which the 256 x 256 tile does not have to spare.
+    static constexpr bool STATIC_STAGES = NW <= 4;
 };
 
 // 256 x 256 workgroup tiles (8 waves of 128 x 64, two LDS stages, one
@@ -438,10 +445,16 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     constexpr int NW = Cfg::NW, TM = Cfg::TM, TN = Cfg::TN, IT = Cfg::IT, JT = Cfg::JT;
     constexpr int A_BYTES = Cfg::A_BYTES, B_BYTES = Cfg::B_BYTES;
     static_assert(TN % 128 == 0 || !BGRAN || TN <= 128, "tile columns within 128-wide weight tiles");
-    constexpr int STAGES = Cfg::STAGES;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES][A_BYTES + B_BYTES];
+    static_assert(Cfg::STAGES == 2, "two LDS stages");
+    // Two stages in distinct LDS objects.  With STATIC_STAGES the K loop names
+    // them only at compile time, so the compiler can tell a stage being filled
+    // by direct copies from the one being read and does not make the reads wait
+    // for the copies in flight.
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[A_BYTES + B_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[A_BYTES + B_BYTES];
     // per stage: A scales [0, TM), B scales from TM on, then unused slots
-    __shared__ __attribute__((aligned(16))) float lds_sc[STAGES][NW * 64];
+    __shared__ __attribute__((aligned(16))) float lds_sc0[NW * 64];
+    __shared__ __attribute__((aligned(16))) float lds_sc1[NW * 64];
     static_assert(TM + TN <= NW * 64, "one scale slot per lane");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -455,10 +468,6 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
 #pragma unroll
             for (int r = 0; r < 4; r++)
                 acc[i][j][r] = 0.0f;
-
-    // vmcnt(n) immediate for gfx9-family s_waitcnt (expcnt and lgkmcnt left unconstrained)
-    constexpr int WAIT_NEWEST = 0x0F70 | (Cfg::LOADS & 15) | ((Cfg::LOADS >> 4) << 14);
-    static_assert(Cfg::LOADS < 64, "vmcnt range");
 
     // K blocks are numbered across the segments, in order: block v of the
     // product is block v - (blocks of the segments before) of its segment.
@@ -489,10 +498,10 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             step = A_KMAJ ? 1 : p.M;
         }
     };
-    auto stage_seg = [&](const KSeg &sg, int64_t kb, const float *sc, int buf) {
+    auto stage_seg = [&](const KSeg &sg, int64_t kb, const float *sc, uint8_t *L, float *LSC) {
         const int64_t k0 = kb * 128;
-        uint8_t *ta = lds[buf];
-        uint8_t *tb = lds[buf] + A_BYTES;
+        uint8_t *ta = L;
+        uint8_t *tb = L + A_BYTES;
         if (A_KMAJ)
             fast_stage_k<TM, NW>(ta, sg.A, sg.lda, m0, k0, wave, lane);
         else
@@ -501,7 +510,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             fast_stage_k<TN, NW>(tb, sg.B, sg.ldb, n0, k0, wave, lane);
         else
             fast_stage_mn<TN, NW>(tb, sg.B, sg.ldb, k0, n0, wave, lane);
-        load_lds4(sc, &lds_sc[buf][wave * 64]);
+        load_lds4(sc, &LSC[wave * 64]);
     };
 
     // One segment (the common case): operands and scale source fixed.
@@ -518,9 +527,9 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     seg_start[1] = MULTI && p.nseg > 1 ? p.seg[0].KB : INT64_MAX;
     seg_start[2] = MULTI && p.nseg > 2 ? seg_start[1] + p.seg[1].KB : INT64_MAX;
     seg_start[3] = MULTI && p.nseg > 3 ? seg_start[2] + p.seg[2].KB : INT64_MAX;
-    auto stage = [&](int64_t v, int buf) {
+    auto stage = [&](int64_t v, uint8_t *L, float *LSC) {
         if (!MULTI) {
-            stage_seg(seg0, v, sc0_base + v * sc0_step, buf);
+            stage_seg(seg0, v, sc0_base + v * sc0_step, L, LSC);
             return;
         }
         const int si = (v >= seg_start[1]) + (v >= seg_start[2]) + (v >= seg_start[3]);
@@ -535,31 +544,22 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
         const float *base;
         int64_t step;
         scale_source(sg, base, step);
-        stage_seg(sg, kb, base + kb * step, buf);
+        stage_seg(sg, kb, base + kb * step, L, LSC);
     };
 
     const int64_t lo = kb_lo, hi = kb_hi;
-    int buf = 0;
-    for (int s = 0; s < STAGES - 1; s++)
-        if (lo + s < hi)
-            stage(lo + s, buf + s < STAGES ? buf + s : buf + s - STAGES);
-    for (int64_t kb = lo; kb < hi; kb++) {
-        // Block kb's copies must have landed.  With three stages, block
-        // kb+1's copies (issued one iteration later) may still be in flight.
-        if (STAGES > 2 && kb + 1 < hi)
-            __builtin_amdgcn_s_waitcnt(WAIT_NEWEST);
-        else
-            __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();   // everyone's copies of block kb have landed; block kb-1 is no longer read
-        if (kb + STAGES - 1 < hi) {
-            int nb_ = buf + STAGES - 1;
-            if (nb_ >= STAGES)
-                nb_ -= STAGES;
-            stage(kb + STAGES - 1, nb_);
-        }
+    if (lo < hi)
+        stage(lo, lds0, lds_sc0);
+    // K block kb computed from stage (L, LSC) while block kb + 1 is copied
+    // into the other stage (LN, LSCN).
+    auto kblock = [&](int64_t kb, const uint8_t *L, const float *LSC, uint8_t *LN, float *LSCN) {
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of block kb have landed
+        __syncthreads();   // everyone's have; block kb-1 (in LN) is no longer read
+        if (kb + 1 < hi)
+            stage(kb + 1, LN, LSCN);
 
-        const uint8_t *ta = lds[buf];
-        const uint8_t *tb = lds[buf] + A_BYTES;
+        const uint8_t *ta = L;
+        const uint8_t *tb = L + A_BYTES;
         const int wrow = wm * IT * 16, wcol = wn * JT * 16;
 
         if constexpr (MX) {
@@ -572,13 +572,13 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             v8i bf[JT];
 #pragma unroll
             for (int j = 0; j < JT; j++) {
-                sbe[j] = e8m0(BGRAN ? lds_sc[buf][TM + (wcol >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)]);
+                sbe[j] = e8m0(BGRAN ? LSC[TM + (wcol >> 7)] : LSC[TM + wcol + j * 16 + (lane & 15)]);
                 bf[j] = B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane) : fast_frag_mn<TN>(tb, wcol + j * 16, lane);
             }
 #pragma unroll
             for (int i = 0; i < IT; i++) {
                 const v8i af = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
-                const int sae = e8m0(lds_sc[buf][wrow + i * 16 + (lane & 15)]);
+                const int sae = e8m0(LSC[wrow + i * 16 + (lane & 15)]);
 #pragma unroll
                 for (int j = 0; j < JT; j++) {
                     v4f c = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
@@ -597,7 +597,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             float sbv[JT];
 #pragma unroll
             for (int j = 0; j < JT; j++)
-                sbv[j] = BGRAN ? lds_sc[buf][TM + (wcol >> 7)] : lds_sc[buf][TM + wcol + j * 16 + (lane & 15)];
+                sbv[j] = BGRAN ? LSC[TM + (wcol >> 7)] : LSC[TM + wcol + j * 16 + (lane & 15)];
 
             V8H4 bh[JT];
 #pragma unroll
@@ -616,7 +616,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             v8i araw = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
 #pragma unroll
             for (int i = 0; i < IT; i++) {
-                const float4 sa4 = *reinterpret_cast<const float4 *>(&lds_sc[buf][wrow + i * 16 + 4 * (lane >> 4)]);
+                const float4 sa4 = *reinterpret_cast<const float4 *>(&LSC[wrow + i * 16 + 4 * (lane >> 4)]);
                 const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
                 float sab[4];
 #pragma unroll
@@ -660,22 +660,34 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                 }
             }
         }
-        buf = (buf + 1 == STAGES) ? 0 : buf + 1;
+    };
+    if constexpr (Cfg::STATIC_STAGES) {
+        for (int64_t kb = lo; kb < hi; kb += 2) {
+            kblock(kb, lds0, lds_sc0, lds1, lds_sc1);
+            if (kb + 1 < hi)
+                kblock(kb + 1, lds1, lds_sc1, lds0, lds_sc0);
+        }
+    } else {
+        // stage chosen at run time: every read of a stage waits for the copies in flight
+        for (int64_t kb = lo; kb < hi; kb++) {
+            const bool odd = ((kb - lo) & 1) != 0;
+            kblock(kb, odd ? lds1 : lds0, odd ? lds_sc1 : lds_sc0, odd ? lds0 : lds1, odd ? lds_sc0 : lds_sc1);
+        }
     }
 
     // Epilogue.  Each wave passes its results through a private LDS strip of
     // 16 rows x JT*16 columns so that every lane stores 16 contiguous bytes of
     // one row (the MFMA layout gives a lane one column of four rows).  The
-    // strips live in stage `buf`, which no wave reads any more: every wave has
-    // passed the last K block's barrier, after which only the last block's
-    // stage can still be in use, and no copy into `buf` is in flight.
+    // strips live in stage 0, free once every wave has finished the last K
+    // block (the barrier below); no copy is in flight by then.
     constexpr int CW = JT * 16;                              // strip width
     constexpr int SST = CW + 4;                              // row stride (floats): 4 row groups hit disjoint banks
     constexpr int CH = (CBF16 && !OUT_PARTIAL) ? 8 : 4;      // elements per 16-byte store
     constexpr int NCH = 16 * CW / CH;                        // 16-byte chunks per strip
     static_assert(NCH % 64 == 0, "whole chunks per lane");
     static_assert(16 * SST * 4 * NW <= A_BYTES + B_BYTES, "strips fit in one stage");
-    float *strip = reinterpret_cast<float *>(lds[buf]) + wave * 16 * SST;
+    __syncthreads();   // every wave is done with the last K block: stage 0 is free
+    float *strip = reinterpret_cast<float *>(lds0) + wave * 16 * SST;
     const int wrow = wm * IT * 16, wcol = wn * JT * 16;
     void *const gC = p.C;
     const int64_t ldc = p.ldc, pM = p.M, pN = p.N;
@@ -854,7 +866,7 @@ constexpr int kComputeUnits = 256;
 // Picks the candidate with the least estimated time.  The estimate uses
 // per-K-block step times measured on gfx950 with every CU busy: a 256 x 256
 // tile (one workgroup per CU) takes about 4.4 us per K block; a 128 x 128 tile
-// about 2.3 us when two share a CU and 1.8 us alone.  Workgroups are spread
+// about 1.9 us when two share a CU and 1.4 us alone.  Workgroups are spread
 // evenly over the CUs, so the busiest CU sets the time.  Splitting K adds
 // the partial sums, (splits + 1) M N 4 bytes moved at about 4 TB/s, and the
 // reduction launch.
@@ -878,9 +890,9 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K, bool mx = false)
             const double steps = (double)((KB + sp - 1) / sp);
             const int64_t per_cu = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
             double us = cfg == CFG_L ? (double)per_cu * steps * 4.4 + 5.0
-                                     : (double)(per_cu / 2) * steps * 2.3 + (double)(per_cu % 2) * steps * 1.8;
-            if (mx)   // no widening or promotion: about half the step time
-                us *= 0.5;
+                                     : (double)(per_cu / 2) * steps * 1.9 + (double)(per_cu % 2) * steps * 1.4;
+            if (mx)   // no widening or promotion: about 0.6 of the step time
+                us *= 0.6;
             if (sp > 1)
                 us += (double)(sp + 1) * (double)M * (double)N * 4.0 / 4e6 + 5.0;
             if (us < best_us) {
@@ -1003,7 +1015,7 @@ double group_estimate(int cfg, const std::vector<GemmArgs> &ps)
     const double per_cu = std::ceil(tiles / kComputeUnits), mean = steps / tiles;
     if (cfg == CFG_L)
         return per_cu * mean * 4.4 + 5.0;
-    return std::floor(per_cu / 2.0) * mean * 2.3 + std::fmod(per_cu, 2.0) * mean * 1.8;
+    return std::floor(per_cu / 2.0) * mean * 1.9 + std::fmod(per_cu, 2.0) * mean * 1.4;
 }
 
 template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
