@@ -132,9 +132,13 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
         keep += [xs, wts, dys]
         # forward: each weight quantised once (128x128 tiles), each distinct input
         # once both ways (the 128-token copy is kept for the weight gradient)
-        for g, n, k, src in synth.LAYER_GEMMS:
-            plan.add(L.puro_fp8_quant_weight, (P(wts[g]), F32, n, k, k, P(qw[g]), k, P(sw[g]), stream_ptr),
-                     "quant_weight", "quant_weight", 0, n * k * (4 + 1) + nb(n) * nb(k) * 4)
+        # (the layer's seven weights in one grouped launch)
+        wd = (pf.QuantWeightDesc * len(synth.LAYER_GEMMS))(
+            *[pf.QuantWeightDesc(P(wts[g]), n, k, k, P(qw[g]), k, P(sw[g])) for g, n, k, _ in synth.LAYER_GEMMS])
+        keep.append(wd)
+        plan.add(L.puro_fp8_quant_weight_grouped, (F32, wd, len(synth.LAYER_GEMMS), stream_ptr),
+                 "quant_weight", "quant_weight", 0,
+                 sum(n * k * (4 + 1) + nb(n) * nb(k) * 4 for _, n, k, _ in synth.LAYER_GEMMS))
         for name, c in synth.LAYER_INPUTS:
             plan.add(L.puro_fp8_quant_dual, (P(xs[name]), BF16, T, c, c, P(qx[name]), c, P(sx[name]), 1,
                                              P(qxt[name]), T, P(sxt[name]), stream_ptr),

@@ -8,6 +8,7 @@ every call raises.
 Names mirror the C entry points:
     puro_fp8_quant_act(x)                 -> (q, s)   1x128 blocks along rows
     puro_fp8_quant_weight(w)              -> (q, s)   128x128 tiles
+    puro_fp8_quant_weight_grouped([w..])  -> [(q, s)..] several weights, one launch
     puro_fp8_quant_transpose(x, t_out)    -> (q, s)   128-token blocks per column
     puro_fp8_quant_dual(x, t_out)         -> both of the above from one read of x
     puro_fp8_gemm(layout, A, sA, B, sB, bgran, out_dtype) -> C
@@ -53,6 +54,12 @@ class GemmDesc(ctypes.Structure):
                 ("seg", GemmSegment * MAX_SEGMENTS), ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
 
 
+class QuantWeightDesc(ctypes.Structure):
+    """puro_quant_weight_desc_t: one weight of puro_fp8_quant_weight_grouped."""
+    _fields_ = [("w", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ldw", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("ldq", ctypes.c_int64), ("s", ctypes.c_void_p)]
+
+
 def gemm_desc(M, N, segments, C, ldc, accumulate=False):
     """GemmDesc from (K, A, lda, sA, B, ldb, sB) tuples of pointers and strides."""
     if not 1 <= len(segments) <= MAX_SEGMENTS:
@@ -94,6 +101,10 @@ def lib():
             f.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp, ctypes.c_size_t, vp]
         L.puro_fp8_gemm_mx_workspace_size.restype = ctypes.c_size_t
         L.puro_fp8_gemm_mx_workspace_size.argtypes = [i32, i64, i64, i64, i32]
+        for name in ("puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [i32, ctypes.POINTER(QuantWeightDesc), i32, vp]
         L.puro_fp8_gemm_grouped.restype = i32
         L.puro_fp8_gemm_grouped.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, vp]
         L.puro_status_string.restype = ctypes.c_char_p
@@ -203,6 +214,37 @@ def puro_fp8_quant_weight(w, q=None, s=None, stream=None, pow2=False):
     _check(fn(_ptr(w), _dtype_code(w), rows, cols, _ld(w), _ptr(q), _ld(q), _ptr(s), _stream(stream)),
            "puro_fp8_quant_weight")
     return q, s
+
+
+def puro_fp8_quant_weight_grouped(weights, outs=None, stream=None, pow2=False):
+    """128x128 tiles of several weights (one dtype) in as few launches as possible.
+
+    weights: list of 2-D tensors; outs: optional list of (q, s) to write into.
+    Returns the list of (q, s), each as puro_fp8_quant_weight would return it.
+    """
+    if outs is None:
+        outs = [(None, None)] * len(weights)
+    if len(outs) != len(weights):
+        raise ValueError("outs must have one (q, s) per weight")
+    if any(w.dtype != weights[0].dtype for w in weights):
+        raise ValueError("all weights must share one dtype")
+    res, descs = [], []
+    for w, (q, s) in zip(weights, outs):
+        rows, cols = w.shape
+        if q is None:
+            q = empty_2d(rows, cols, torch.uint8, w.device)
+        if s is None:
+            s = torch.empty((_nblk(rows), _nblk(cols)), dtype=torch.float32, device=w.device)
+        _need(q, (rows, cols), torch.uint8, "q")
+        _need_dense(s, (_nblk(rows), _nblk(cols)), "s")
+        descs.append(QuantWeightDesc(_ptr(w), rows, cols, _ld(w), _ptr(q), _ld(q), _ptr(s)))
+        res.append((q, s))
+    if not descs:
+        return res
+    arr = (QuantWeightDesc * len(descs))(*descs)
+    fn = lib().puro_fp8_quant_weight_grouped_pow2 if pow2 else lib().puro_fp8_quant_weight_grouped
+    _check(fn(_dtype_code(weights[0]), arr, len(descs), _stream(stream)), "puro_fp8_quant_weight_grouped")
+    return res
 
 
 def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None, pow2=False):

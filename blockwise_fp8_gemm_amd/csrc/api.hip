@@ -85,6 +85,35 @@ static puro_status_t quant_weight_impl(const void *w, puro_dtype_t wdt, int64_t 
     }
 }
 
+static puro_status_t quant_weight_grouped_impl(puro_dtype_t wdt, const puro_quant_weight_desc_t *items,
+                                               int count, bool pow2, hipStream_t stream)
+{
+    try {
+        if (wdt != PURO_F32 && wdt != PURO_BF16)
+            return PURO_ERR_ENUM;
+        if (count < 0 || count > PURO_QUANT_MAX_GROUP)
+            return PURO_ERR_SHAPE;
+        if (count > 0 && !items)
+            return PURO_ERR_NULL;
+        std::vector<puro::QuantWeightItem> v;
+        v.reserve((size_t)count);
+        for (int i = 0; i < count; i++) {
+            const puro_quant_weight_desc_t &d = items[i];
+            const puro_status_t st = check_quant(d.w, wdt, d.rows, d.cols, d.ldw, d.q, d.ldq, d.cols, d.s);
+            if (st != PURO_OK)
+                return st;
+            if (d.rows == 0 || d.cols == 0)
+                continue;
+            v.push_back({d.w, d.rows, d.cols, d.ldw, d.q, d.ldq, d.s, (d.cols + 127) / 128});
+        }
+        if (v.empty())
+            return PURO_OK;
+        return from_hip(puro::launch_quant_weight_group(v.data(), (int)v.size(), wdt == PURO_BF16, pow2, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
 static puro_status_t quant_transpose_impl(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
                                           int64_t ldx, int transpose_out, uint8_t *q, int64_t ldq, float *s,
                                           bool pow2, hipStream_t stream)
@@ -163,6 +192,18 @@ puro_status_t puro_fp8_quant_act_pow2(const void *x, puro_dtype_t xdt, int64_t r
                                       uint8_t *q, int64_t ldq, float *s, hipStream_t stream)
 {
     return quant_act_impl(x, xdt, rows, cols, ldx, q, ldq, s, true, stream);
+}
+
+puro_status_t puro_fp8_quant_weight_grouped(puro_dtype_t wdt, const puro_quant_weight_desc_t *items, int count,
+                                            hipStream_t stream)
+{
+    return quant_weight_grouped_impl(wdt, items, count, false, stream);
+}
+
+puro_status_t puro_fp8_quant_weight_grouped_pow2(puro_dtype_t wdt, const puro_quant_weight_desc_t *items,
+                                                 int count, hipStream_t stream)
+{
+    return quant_weight_grouped_impl(wdt, items, count, true, stream);
 }
 
 puro_status_t puro_fp8_quant_weight_pow2(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,

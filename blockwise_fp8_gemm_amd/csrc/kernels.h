@@ -14,6 +14,19 @@ hipError_t launch_quant_act(const void *x, bool bf16, int64_t rows, int64_t cols
                             uint8_t *q, int64_t ldq, float *s, bool pow2, hipStream_t st);
 hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t cols, int64_t ldw,
                                uint8_t *q, int64_t ldq, float *s, bool pow2, hipStream_t st);
+// One weight of a grouped weight quantisation (as launch_quant_weight's
+// arguments; cb = number of 128-column tiles).
+struct QuantWeightItem {
+    const void *w;
+    int64_t rows, cols, ldw;
+    uint8_t *q;
+    int64_t ldq;
+    float *s;
+    int64_t cb;
+};
+constexpr int kQuantGroupMax = 16;   // weights per launch; more take several launches
+hipError_t launch_quant_weight_group(const QuantWeightItem *items, int count, bool bf16, bool pow2,
+                                     hipStream_t st);
 hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int64_t cols,
                                   int64_t ldx, bool transpose_out, uint8_t *q, int64_t ldq,
                                   float *s, bool pow2, hipStream_t st);

@@ -92,16 +92,17 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const T *__restrict__ x,
 // 8*(t%16) .. +7 of rows t/16 and t/16 + 64: 16 values in registers.  amax:
 // cross-lane max per wave, then across the 16 waves through LDS.
 // ---------------------------------------------------------------------------
+// Tile (tx, ty) of one weight: columns [128 tx, +128) x rows [128 ty, +128).
 template <typename T>
-__global__ __launch_bounds__(1024) void quant_weight_kernel(const T *__restrict__ w, int64_t rows,
-                                                            int64_t cols, int64_t ldw,
-                                                            uint8_t *__restrict__ q, int64_t ldq,
-                                                            float *__restrict__ s, int64_t cb, int pow2)
+__device__ __forceinline__ void quant_weight_tile(const T *__restrict__ w, int64_t rows, int64_t cols,
+                                                  int64_t ldw, uint8_t *__restrict__ q, int64_t ldq,
+                                                  float *__restrict__ s, int64_t cb, int64_t tx,
+                                                  int64_t ty, int pow2)
 {
     __shared__ float red[16];
     const int t = threadIdx.x;
     const int cc = t & 15, rg = t >> 4;
-    const int64_t r0 = (int64_t)blockIdx.y * 128, cbase = (int64_t)blockIdx.x * 128;
+    const int64_t r0 = ty * 128, cbase = tx * 128;
     const int64_t c0 = cbase + cc * 8;
     const bool full_tile = (r0 + 128 <= rows) && (cbase + 128 <= cols);
 
@@ -153,7 +154,41 @@ __global__ __launch_bounds__(1024) void quant_weight_kernel(const T *__restrict_
         }
     }
     if (t == 0)
-        s[blockIdx.y * cb + blockIdx.x] = sc;
+        s[ty * cb + tx] = sc;
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void quant_weight_kernel(const T *__restrict__ w, int64_t rows,
+                                                            int64_t cols, int64_t ldw,
+                                                            uint8_t *__restrict__ q, int64_t ldq,
+                                                            float *__restrict__ s, int64_t cb, int pow2)
+{
+    quant_weight_tile<T>(w, rows, cols, ldw, q, ldq, s, cb, blockIdx.x, blockIdx.y, pow2);
+}
+
+// Several weights in one launch: weight i owns workgroups [first[i], first[i+1]),
+// one per tile, row-major over its tiles.
+struct QuantWeightGroup {
+    QuantWeightItem it[kQuantGroupMax];
+    int first[kQuantGroupMax + 1];
+    int count;
+    int pow2;
+};
+
+template <typename T>
+__global__ __launch_bounds__(1024) void quant_weight_group_kernel(QuantWeightGroup args)
+{
+    (void)args;   // read through the argument segment pointer: no copy to scratch memory
+    typedef __attribute__((address_space(4))) const QuantWeightGroup *KernargQ;
+    const KernargQ g = (KernargQ)__builtin_amdgcn_kernarg_segment_ptr();
+    const int b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < g->count && b >= g->first[i + 1])
+        i++;
+    i = __builtin_amdgcn_readfirstlane(i);   // uniform: the item's fields stay in scalar registers
+    const int64_t local = b - g->first[i], cb = g->it[i].cb;
+    quant_weight_tile<T>((const T *)g->it[i].w, g->it[i].rows, g->it[i].cols, g->it[i].ldw, g->it[i].q,
+                         g->it[i].ldq, g->it[i].s, cb, local % cb, local / cb, g->pow2);
 }
 
 // ---------------------------------------------------------------------------
@@ -684,6 +719,36 @@ hipError_t launch_quant_weight(const void *w, bool bf16, int64_t rows, int64_t c
         hipLaunchKernelGGL(quant_weight_kernel<float>, grid, dim3(1024), 0, st, (const float *)w,
                            rows, cols, ldw, q, ldq, s, cb, (int)pow2);
     return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_group(const QuantWeightItem *items, int count, bool bf16, bool pow2,
+                                     hipStream_t st)
+{
+    for (int lo = 0; lo < count; lo += kQuantGroupMax) {
+        QuantWeightGroup g;
+        g.count = 0;
+        g.first[0] = 0;
+        g.pow2 = pow2 ? 1 : 0;
+        for (int i = lo; i < count && g.count < kQuantGroupMax; i++) {
+            const int64_t tiles = ((items[i].rows + 127) / 128) * items[i].cb;
+            if (tiles == 0)
+                continue;   // empty weight: nothing to do
+            g.it[g.count] = items[i];
+            g.first[g.count + 1] = g.first[g.count] + (int)tiles;
+            g.count++;
+        }
+        if (g.count == 0)
+            continue;
+        const dim3 grid((unsigned)g.first[g.count]);
+        if (bf16)
+            hipLaunchKernelGGL(quant_weight_group_kernel<uint16_t>, grid, dim3(1024), 0, st, g);
+        else
+            hipLaunchKernelGGL(quant_weight_group_kernel<float>, grid, dim3(1024), 0, st, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int64_t cols,

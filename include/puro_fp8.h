@@ -100,6 +100,30 @@ puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t row
                                     hipStream_t stream);
 
 /*
+ * Grouped weight quantiser: `count` weights, each exactly as in
+ * puro_fp8_quant_weight (same codes, scales and layouts), in as few launches
+ * as possible.  Their tiles run side by side, which fills the GPU where one
+ * weight alone does not: e.g. all projections of a layer, or every weight of a
+ * model after an optimizer step, at once.
+ *   wdt    element type of every weight (FP32 or BF16)
+ *   items  HOST array of `count` descriptors, read before the call returns
+ *   count  0 .. PURO_QUANT_MAX_GROUP (0: nothing is enqueued; more: PURO_ERR_SHAPE)
+ * Every item is validated as a puro_fp8_quant_weight call before anything is
+ * enqueued, and the first failing item's status is returned.  No output may
+ * overlap another item's output or any input.
+ */
+#define PURO_QUANT_MAX_GROUP 4096
+typedef struct {
+    const void *w;            /* [rows][cols], row stride ldw */
+    int64_t rows, cols, ldw;
+    uint8_t *q;               /* [rows][cols] codes, row stride ldq */
+    int64_t ldq;
+    float *s;                 /* [ceil(rows/128)][ceil(cols/128)], dense */
+} puro_quant_weight_desc_t;
+puro_status_t puro_fp8_quant_weight_grouped(puro_dtype_t wdt, const puro_quant_weight_desc_t *items,
+                                            int count, hipStream_t stream);
+
+/*
  * Token-dimension quantiser for the weight-gradient GEMM: blocks are 128
  * consecutive tokens of one column of x [tokens][cols] (FP32 or BF16, stride ldx).
  *   transpose_out = 1: q [cols][tokens] (stride ldq), s [cols][ceil(tokens/128)]
@@ -235,6 +259,8 @@ puro_status_t puro_fp8_quant_act_pow2(const void *x, puro_dtype_t xdt, int64_t r
                                       uint8_t *q, int64_t ldq, float *s, hipStream_t stream);
 puro_status_t puro_fp8_quant_weight_pow2(const void *w, puro_dtype_t wdt, int64_t rows, int64_t cols,
                                          int64_t ldw, uint8_t *q, int64_t ldq, float *s, hipStream_t stream);
+puro_status_t puro_fp8_quant_weight_grouped_pow2(puro_dtype_t wdt, const puro_quant_weight_desc_t *items,
+                                                 int count, hipStream_t stream);
 puro_status_t puro_fp8_quant_transpose_pow2(const void *x, puro_dtype_t xdt, int64_t tokens, int64_t cols,
                                             int64_t ldx, int transpose_out, uint8_t *q, int64_t ldq, float *s,
                                             hipStream_t stream);

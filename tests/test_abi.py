@@ -34,6 +34,7 @@ def test_header_declares_the_calls():
               "puro_fp8_quant_dual", "puro_fp8_quant_act_pow2", "puro_fp8_quant_weight_pow2",
               "puro_fp8_quant_transpose_pow2", "puro_fp8_quant_dual_pow2", "puro_fp8_gemm_mx",
               "puro_fp8_gemm_mx_workspace_size", "puro_status_string",
+              "puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2",
               "puro_fp8_version"):
         assert n in names
 
@@ -230,3 +231,30 @@ def test_gemm_mx_validation():
     assert _gmx(M=0, A=NUL, sA=NUL, C=NUL) == OK
     assert pf.puro_fp8_gemm_mx_workspace_size("NT", 200, 256, 256, "1x128") == 0
     assert pf.puro_fp8_gemm_mx_workspace_size("NT", 256, 256, 8192, "1x128") >= 0
+
+
+@pytest.mark.parametrize("name", ["puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2"])
+def test_quant_weight_grouped_validation(name):
+    fn = getattr(pf.lib(), name)
+    D = pf.QuantWeightDesc
+
+    def call(items, dt=0, count=None):
+        arr = (D * max(len(items), 1))(*items)
+        return fn(dt, arr, len(items) if count is None else count, None)
+
+    good = D(P, 256, 256, 256, P, 256, P)
+    empty = D(NUL, 0, 256, 256, NUL, 256, NUL)
+    assert call([]) == OK
+    assert call([empty, empty]) == OK                     # nothing to do: no launch
+    assert call([good], dt=7) == ENUM
+    assert call([good], count=-1) == SHAPE
+    assert call([good], count=4097) == SHAPE
+    assert fn(0, None, 1, None) == NULL
+    # the first failing item decides, and nothing is enqueued before validation ends
+    assert call([good, D(P, 256, 256, 100, P, 256, P)]) == SHAPE        # ldw < cols
+    assert call([good, D(P, 256, 256, 264, P, 256, P)]) == ALIGN        # ldw not a multiple of 16
+    assert call([good, D(P_ODD, 256, 256, 256, P, 256, P)]) == ALIGN    # w not 16-byte aligned
+    assert call([good, D(NUL, 256, 256, 256, P, 256, P)]) == NULL
+    assert call([good, D(P, 256, 256, 256, P, 256, NUL)]) == NULL
+    assert call([D(P, -1, 256, 256, P, 256, P), D(NUL, 4, 4, 16, P, 16, P)]) == SHAPE
+

@@ -162,8 +162,8 @@ def _check_sampled_sum(layout, bgran, segs, C, seed, out):
 
 def test_layer_grouped_full_size(dev):
     """One whole layer at 8,192 tokens in the grouped launches the benchmark times: every
-    input and output gradient quantised both ways in one read (byte-compared over the whole
-    tensors), the forward products grouped (q/k/v, o, gate/up, down), the data gradients
+    input and output gradient quantised both ways in one read and the seven weights in one
+    launch (byte-compared over the whole tensors), the forward products grouped (q/k/v, o, gate/up, down), the data gradients
     summed per input (K segments), and the seven weight gradients in one launch."""
     T = synth.TOKENS
     shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
@@ -179,12 +179,16 @@ def test_layer_grouped_full_size(dev):
 
     for i, (name, c) in enumerate(synth.LAYER_INPUTS):
         dual(name, synth.normal((T, c), 1.0, synth.seed_of(4, 0, i), "bf16"))
+    Ws = {}
     for j, (g, n, k, src) in enumerate(synth.LAYER_GEMMS):
         dual("dY_" + g, synth.normal((T, n), 1e-3, synth.seed_of(4, 0, 20 + j), "bf16"))
-        W = synth.normal((n, k), 0.02, synth.seed_of(4, 0, 10 + j))
-        qw, sw = pf.puro_fp8_quant_weight(to_dev(W))
-        rw = oracle.quant_weight(W)
-        torch.cuda.synchronize()
+        Ws[g] = synth.normal((n, k), 0.02, synth.seed_of(4, 0, 10 + j))
+    # the layer's seven weights in one grouped launch, as the benchmark does
+    gs = [g for g, _, _, _ in synth.LAYER_GEMMS]
+    qws = pf.puro_fp8_quant_weight_grouped([to_dev(Ws[g]) for g in gs])
+    torch.cuda.synchronize()
+    for g, (qw, sw) in zip(gs, qws):
+        rw = oracle.quant_weight(Ws[g])
         _same(qw, rw[0], ("qW", g))
         _same(sw, rw[1], ("sW", g))
         host_q["W_" + g], dev_q["W_" + g] = rw, (qw, sw)

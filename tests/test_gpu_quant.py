@@ -107,6 +107,37 @@ def test_quant_weight_bit_exact(dev, name, make, ld):
     _assert_same(q, s, q_ref, s_ref, name)
 
 
+@pytest.mark.parametrize("rule", ["amax", "pow2"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_weight_grouped_bit_exact(dev, dtype, rule):
+    """Several weights in grouped launches: each equal to the oracle's weight quantiser.
+
+    21 weights (two launches of at most 16): a layer's seven projections at
+    reduced size, ragged extents with padded rows, an adversarial weight and
+    empty ones in between.
+    """
+    def f(x):
+        return synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    shapes = [(512, 256), (256, 256), (256, 256), (256, 256), (768, 256), (768, 256), (256, 768),
+              (200, 333), (129, 130), (1, 16), (128, 128), (0, 256), (384, 640), (256, 0)]
+    ws, lds = [], []
+    for i, (r, c) in enumerate(shapes):
+        ws.append(f(synth.normal((r, c), 0.02, 5200 + i)))
+        lds.append((c + 15) // 16 * 16 + (16 if i % 3 == 0 else 0))
+    ws.append(f(_adversarial(256, 512, 5250)))
+    lds.append(512)
+    for i in range(6):
+        ws.append(f(synth.normal((128 * (i + 1), 128), 1.0 + i, 5260 + i)))
+        lds.append(128)
+    devs = [to_dev(w, ld=ld) for w, ld in zip(ws, lds)]
+    outs = pf.puro_fp8_quant_weight_grouped(devs, pow2=(rule == "pow2"))
+    torch.cuda.synchronize()
+    assert len(outs) == len(ws) == 21
+    for i, (w, (q, s_)) in enumerate(zip(ws, outs)):
+        q_ref, s_ref = oracle.quant_weight(w, rule=rule)
+        _assert_same(q, s_, q_ref, s_ref, "grouped weight %d %s" % (i, w.shape))
+
+
 TRANSPOSE_CASES = [
     ("layer_x_bf16", lambda: synth.normal((1024, 2048), 1.0, synth.seed_of(3, 0, 0), "bf16"), None),
     ("dy_bf16", lambda: synth.normal((1024, 1024), 1e-3, synth.seed_of(3, 0, 9), "bf16"), None),
