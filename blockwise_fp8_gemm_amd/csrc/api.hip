@@ -343,7 +343,7 @@ puro_status_t puro_fp8_gemm_mx(puro_layout_t layout, int64_t M, int64_t N, int64
             return st;
         if (M == 0 || N == 0)
             return PURO_OK;
-        if (!mx_aligned(M, N, K))
+        if (!mx_aligned(M, N, K) || lda >= ((int64_t)1 << 28) || ldb >= ((int64_t)1 << 28))
             return PURO_ERR_SHAPE;
         puro::GemmProblem p = make_problem(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
         const size_t need = puro::gemm_mx_workspace_bytes(p);

@@ -302,6 +302,11 @@ __device__ __forceinline__ void load_lds4(const void *g, void *lds_wave_base)
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_wave_base, 4, 0, 0);
 }
 
+// The copies below address global memory as a wave-uniform base (scalar
+// registers: the wave number is uniform) plus a 32-bit per-lane offset of at
+// most 7 rows (the fast path needs leading dimensions below 2^28), so that
+// the per-block address arithmetic runs on the scalar unit.
+
 // Rows [row0, row0+ROWS) x bytes [k0, k0+128) of a K-contiguous operand, NW waves.
 template <int ROWS, int NW>
 __device__ __forceinline__ void fast_stage_k(uint8_t *t, const uint8_t *g, int64_t ld, int64_t row0,
@@ -310,10 +315,14 @@ __device__ __forceinline__ void fast_stage_k(uint8_t *t, const uint8_t *g, int64
     static_assert((ROWS / 8) % NW == 0, "whole 1 KB chunks per wave");
 #pragma unroll
     for (int it = 0; it < ROWS / 8 / NW; it++) {
-        const int c = wave + NW * it;
-        const int row = c * 8 + (lane >> 3);
-        const int seg = (lane & 7) ^ ((row >> 1) & 7);
-        load_lds16(g + (row0 + row) * ld + k0 + seg * 16, t + c * 1024);
+        const int c = wave + NW * it;   // rows 8c .. 8c+7, lane's row 8c + lane / 8
+        const int seg = (lane & 7) ^ ((4 * c + (lane >> 4)) & 7);   // swizzle of that row
+        const uint8_t *base = g + (row0 + 8 * c) * ld + k0;
+        const uint32_t off = (uint32_t)(lane >> 3) * (uint32_t)ld + (uint32_t)(seg * 16);
+        // opaque scalar base: the compiler cannot re-associate it with the lane
+        // offset into a 64-bit per-lane address, and emits the base + offset form
+        asm volatile("" : "+s"(base));
+        load_lds16(base + off, t + c * 1024);
     }
 }
 
@@ -326,10 +335,12 @@ __device__ __forceinline__ void fast_stage_mn(uint8_t *t, const uint8_t *g, int6
     static_assert((128 / RPC) % NW == 0, "whole 1 KB chunks per wave");
 #pragma unroll
     for (int it = 0; it < 128 / RPC / NW; it++) {
-        const int c = wave + NW * it;
-        const int row = c * RPC + lane / SEGS;
-        const int seg = (lane % SEGS) ^ (row & 7);
-        load_lds16(g + (k0 + row) * ld + mn0 + seg * 16, t + c * 1024);
+        const int c = wave + NW * it;   // rows RPC c .. RPC c + RPC - 1
+        const int seg = (lane % SEGS) ^ ((c * RPC + lane / SEGS) & 7);
+        const uint8_t *base = g + (k0 + RPC * c) * ld + mn0;
+        const uint32_t off = (uint32_t)(lane / SEGS) * (uint32_t)ld + (uint32_t)(seg * 16);
+        asm volatile("" : "+s"(base));   // as in fast_stage_k
+        load_lds16(base + off, t + c * 1024);
     }
 }
 
@@ -457,7 +468,8 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     __shared__ __attribute__((aligned(16))) float lds_sc1[NW * 64];
     static_assert(TM + TN <= NW * 64, "one scale slot per lane");
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave-level addresses scalar
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
     float acc[IT][JT][4];
@@ -925,6 +937,17 @@ hipError_t launch_fast_cfg(const GemmArgs &a, int splits, float *ws, hipStream_t
     return hipGetLastError();
 }
 
+// The tile kernel's copies take a 32-bit per-lane offset of up to 7 leading
+// dimensions: every segment's leading dimensions must be below 2^28.
+constexpr int64_t kFastLdLimit = (int64_t)1 << 28;
+bool fast_ld_ok(const GemmArgs &a)
+{
+    bool ok = true;
+    for (int i = 0; i < a.nseg; i++)
+        ok = ok && a.seg[i].lda < kFastLdLimit && a.seg[i].ldb < kFastLdLimit;
+    return ok;
+}
+
 template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_fast(const GemmArgs &a, const FastPlan &plan, float *ws, hipStream_t st)
 {
@@ -937,7 +960,7 @@ template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_one(const GemmArgs &a, float *ws, hipStream_t st)
 {
     const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K);
-    if (plan.ok)
+    if (plan.ok && fast_ld_ok(a))
         return launch_fast<LAYOUT, BGRAN, CBF16>(a, plan, ws, st);
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
     hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
@@ -948,8 +971,8 @@ template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_mx_t(const GemmArgs &a, float *ws, hipStream_t st)
 {
     const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K, true);
-    if (!plan.ok)
-        return hipErrorInvalidValue;   // the API layer admits aligned shapes only
+    if (!plan.ok || !fast_ld_ok(a))
+        return hipErrorInvalidValue;   // the API layer admits aligned shapes and leading dimensions only
     return launch_fast_cfg<CfgQ, LAYOUT, BGRAN, CBF16, true>(a, plan.splits, ws, st);
 }
 
@@ -1062,7 +1085,7 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
         bool k_aligned = true;
         for (int j = 0; j < p.nseg; j++)
             k_aligned = k_aligned && p.seg[j].K % 128 == 0;
-        if (k_aligned && p.M % CfgQ::TM == 0 && p.N % CfgQ::TN == 0) {
+        if (k_aligned && p.M % CfgQ::TM == 0 && p.N % CfgQ::TN == 0 && fast_ld_ok(make_args(p))) {
             fast.push_back(make_args(p));
             all_l = all_l && p.M % CfgL::TM == 0 && p.N % CfgL::TN == 0;
         } else {

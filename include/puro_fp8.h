@@ -275,8 +275,8 @@ puro_status_t puro_fp8_quant_dual_pow2(const void *x, puro_dtype_t xdt, int64_t 
  *   - sA and sB must hold powers of two in [2^-127, 2^127] (as written by the
  *     _pow2 quantisers): only their exponents reach the matrix cores, so any
  *     other value gives wrong results.
- *   - M, N and K must be multiples of 128 (else PURO_ERR_SHAPE; empty
- *     products are allowed and do nothing).
+ *   - M, N and K must be multiples of 128, and lda and ldb below 2^28 (else
+ *     PURO_ERR_SHAPE; empty products are allowed and do nothing).
  * Precision: the FP8 matrix cores add each run of 8 consecutive products in
  * fixed point, dropping bits more than about 13 binary places below the
  * run's largest product (measured on gfx950), so the result is not FP32-exact
