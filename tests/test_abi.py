@@ -227,6 +227,9 @@ def test_gemm_mx_validation():
     assert _gmx(N=136, ldb=256, ldc=256) == SHAPE
     assert _gmx(K=192) == SHAPE
     assert _gmx(K=0, A=NUL, sA=NUL, B=NUL, sB=NUL) == SHAPE
+    # leading dimensions of A and B below 2^28 (the tile kernel's 32-bit lane offsets)
+    assert _gmx(lda=1 << 28) == SHAPE
+    assert _gmx(ldb=1 << 28) == SHAPE
     # empty outputs: nothing enqueued
     assert _gmx(M=0, A=NUL, sA=NUL, C=NUL) == OK
     assert pf.puro_fp8_gemm_mx_workspace_size("NT", 200, 256, 256, "1x128") == 0
