@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
 // K block.  The block's scales travel the same way (4-byte direct loads).
 //
 // LDS layouts (bank-conflict-free fragment reads):
-//   K-major tile [rows][128 B]: segment s of row r at s ^ ((r >> 1) & 7)
+//   K-major tile [rows][128 B]: segment s of row r at s ^ (r & 7) ^ ((r >> 3) & 1)
 //   MN-major tile [128 k][W B]: segment s of row k at s ^ (k & 7)
 // ===========================================================================
 
@@ -302,6 +302,16 @@ __device__ __forceinline__ void load_lds4(const void *g, void *lds_wave_base)
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_wave_base, 4, 0, 0);
 }
 
+// Swizzle of K-major stages: 16-byte segment s of row r sits at s ^ kswz(r).
+// A fragment read (lane i: row base + i % 16, 16 bytes) then touches 16
+// different 16-byte bank groups in every 16 consecutive lanes and 8 in every
+// 8, so it is conflict-free whether the LDS serves 8 or 16 lanes of a
+// 16-byte read per cycle.
+__device__ __forceinline__ int kswz(int row)
+{
+    return (row & 7) ^ ((row >> 3) & 1);
+}
+
 // The copies below address global memory as a wave-uniform base (scalar
 // registers: the wave number is uniform) plus a 32-bit per-lane offset of at
 // most 7 rows (the fast path needs leading dimensions below 2^28), so that
@@ -316,7 +326,7 @@ __device__ __forceinline__ void fast_stage_k(uint8_t *t, const uint8_t *g, int64
 #pragma unroll
     for (int it = 0; it < ROWS / 8 / NW; it++) {
         const int c = wave + NW * it;   // rows 8c .. 8c+7, lane's row 8c + lane / 8
-        const int seg = (lane & 7) ^ ((4 * c + (lane >> 4)) & 7);   // swizzle of that row
+        const int seg = (lane & 7) ^ (((lane >> 3) & 7) ^ (c & 1));   // kswz(8c + lane / 8)
         const uint8_t *base = g + (row0 + 8 * c) * ld + k0;
         const uint32_t off = (uint32_t)(lane >> 3) * (uint32_t)ld + (uint32_t)(seg * 16);
         // opaque scalar base: the compiler cannot re-associate it with the lane
@@ -347,7 +357,7 @@ __device__ __forceinline__ void fast_stage_mn(uint8_t *t, const uint8_t *g, int6
 __device__ __forceinline__ v8i fast_frag_k(const uint8_t *t, int row_base, int lane)
 {
     const int row = row_base + (lane & 15);
-    const int g = lane >> 4, f = (row >> 1) & 7;
+    const int g = lane >> 4, f = kswz(row);
     // whole 16-byte vector loads (not four dword loads merged later), which
     // keeps each read's LDS object visible to the compiler
     const v4i lo = *reinterpret_cast<const v4i *>(t + (row * 128 + (((2 * g) ^ f) << 4)));
