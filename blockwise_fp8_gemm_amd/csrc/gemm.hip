@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
 //
 // LDS layouts (bank-conflict-free fragment reads):
 //   K-major tile [rows][128 B]: segment s of row r at s ^ (r & 7) ^ ((r >> 3) & 1)
-//   MN-major tile [128 k][W B]: segment s of row k at s ^ (k & 7)
+//   MN-major tile [128 k][W B]: segment s of row k at s ^ mnswz<W>(k)
 // ===========================================================================
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -310,6 +310,19 @@ __device__ __forceinline__ void load_lds4(const void *g, void *lds_wave_base)
 __device__ __forceinline__ int kswz(int row)
 {
     return (row & 7) ^ ((row >> 3) & 1);
+}
+
+// Swizzle of M- or N-contiguous stages ([128 k][W bytes]): segment s of row k
+// sits at s ^ mnswz(k).  A transposed fragment read covers 8 consecutive rows
+// per 16 lanes, and the next 16 lanes the rows 32 further on, which the
+// (k & 7) term alone would put on the same banks; bit 5 of k moves them to
+// the other half of each row's segments (bit 0 for 128-byte rows, bit 3 for
+// 256-byte rows).
+template <int W>
+__device__ __forceinline__ int mnswz(int k)
+{
+    static_assert(W == 128 || W == 256, "stage widths of the tile configurations");
+    return (k & 7) ^ (((k >> 5) & 1) << (W == 128 ? 0 : 3));
 }
 
 // The copies below address global memory as a wave-uniform base (scalar
@@ -346,7 +359,7 @@ __device__ __forceinline__ void fast_stage_mn(uint8_t *t, const uint8_t *g, int6
 #pragma unroll
     for (int it = 0; it < 128 / RPC / NW; it++) {
         const int c = wave + NW * it;   // rows RPC c .. RPC c + RPC - 1
-        const int seg = (lane % SEGS) ^ ((c * RPC + lane / SEGS) & 7);
+        const int seg = (lane % SEGS) ^ mnswz<W>(c * RPC + lane / SEGS);
         const uint8_t *base = g + (k0 + RPC * c) * ld + mn0;
         const uint32_t off = (uint32_t)(lane / SEGS) * (uint32_t)ld + (uint32_t)(seg * 16);
         asm volatile("" : "+s"(base));   // as in fast_stage_k
@@ -376,7 +389,7 @@ __device__ __forceinline__ v8i fast_frag_mn(const uint8_t *t, int col_base, int 
         const int k = 32 * g + 8 * q + (i >> 1);
         // one offset added to the stage pointer (not a chain of pointer
         // additions), which keeps the read's LDS object visible to the compiler
-        const uint8_t *a = t + (k * W + ((seg ^ (k & 7)) << 4) + within);
+        const uint8_t *a = t + (k * W + ((seg ^ mnswz<W>(k)) << 4) + within);
         const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)a);
         r[2 * q] = v[0];
         r[2 * q + 1] = v[1];
