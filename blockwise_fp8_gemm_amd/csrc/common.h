@@ -93,11 +93,21 @@ __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d_, 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// Round to nearest even FP32 -> BF16 (finite inputs), as a 16-bit pattern.
+// Round to nearest even FP32 -> BF16, two at a time: a in the low half, b in
+// the high half.  v_cvt_pk_bf16_f32 was checked on gfx950 against an integer
+// round-to-nearest-even for every non-NaN FP32 bit pattern (no mismatch).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t to_bf16x2(float a, float b)
+{
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// One value: the low half of to_bf16x2.
 __device__ __forceinline__ uint16_t to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    return (uint16_t)(to_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
 // Element loads widened to FP32.

@@ -758,10 +758,10 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                     b.x += bf16_lo(c.z); b.y += bf16_hi(c.z); b.z += bf16_lo(c.w); b.w += bf16_hi(c.w);
                 }
                 uint4 o;
-                o.x = (uint32_t)to_bf16(a.x) | ((uint32_t)to_bf16(a.y) << 16);
-                o.y = (uint32_t)to_bf16(a.z) | ((uint32_t)to_bf16(a.w) << 16);
-                o.z = (uint32_t)to_bf16(b.x) | ((uint32_t)to_bf16(b.y) << 16);
-                o.w = (uint32_t)to_bf16(b.z) | ((uint32_t)to_bf16(b.w) << 16);
+                o.x = to_bf16x2(a.x, a.y);
+                o.y = to_bf16x2(a.z, a.w);
+                o.z = to_bf16x2(b.x, b.y);
+                o.w = to_bf16x2(b.z, b.w);
                 *dst = o;
             } else {
                 float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(gC) + m * ldc + n);
@@ -881,8 +881,8 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(const float *__restrict
         sum.w += v.w;
     }
     if (CBF16) {
-        const uint32_t lo = (uint32_t)to_bf16(sum.x) | ((uint32_t)to_bf16(sum.y) << 16);
-        const uint32_t hi = (uint32_t)to_bf16(sum.z) | ((uint32_t)to_bf16(sum.w) << 16);
+        const uint32_t lo = to_bf16x2(sum.x, sum.y);
+        const uint32_t hi = to_bf16x2(sum.z, sum.w);
         *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(C) + m * ldc + n) = make_uint2(lo, hi);
     } else {
         *reinterpret_cast<float4 *>(reinterpret_cast<float *>(C) + m * ldc + n) = sum;
