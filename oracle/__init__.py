@@ -66,6 +66,9 @@ def _lib():
         lib.ref_bf16_rne.restype = ctypes.c_uint16
         lib.ref_bf16_rne.argtypes = [ctypes.c_double]
         lib.ref_bf16_rne_array.argtypes = [_p, _i64, _p]
+        lib.ref_swiglu.restype = ctypes.c_double
+        lib.ref_swiglu.argtypes = [ctypes.c_double, ctypes.c_double]
+        lib.ref_swiglu_array.argtypes = [_p, _p, _i64, _p]
         lib.ref_num_threads.restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -244,3 +247,32 @@ def bf16_rne(values):
     out = np.empty(v.shape, dtype=np.uint16)
     _lib().ref_bf16_rne_array(_ptr(v), v.size, _ptr(out))
     return out
+
+
+# --------------------------------------------------------------------------- gated activation
+
+def _as_f64(x):
+    x = np.asarray(x)
+    if x.dtype == np.uint16:   # BF16 bit patterns
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def swiglu(gate, up):
+    """h = silu(gate) * up = gate * up / (1 + exp(-gate)) in FP64, elementwise.
+
+    The gated feed-forward unit of the Qwen3-1.7B configuration that the model card's
+    configuration table names (SwiGLU with Swish parameter 1; a reading, the pages do not
+    state the activation).  gate and up are float arrays or BF16 bit patterns (uint16)."""
+    g = np.ascontiguousarray(_as_f64(gate))
+    u = np.ascontiguousarray(_as_f64(up))
+    if g.shape != u.shape:
+        raise ValueError("gate and up shapes differ: %s vs %s" % (g.shape, u.shape))
+    out = np.empty(g.shape, dtype=np.float64)
+    _lib().ref_swiglu_array(_ptr(g), _ptr(u), g.size, _ptr(out))
+    return out
+
+
+def swiglu_bf16(gate, up):
+    """The BF16 activation tensor: swiglu() rounded once to the nearest BF16 (ties to even)."""
+    return bf16_rne(swiglu(gate, up))

@@ -503,6 +503,30 @@ void ref_bf16_rne_array(const double *v, int64_t n, uint16_t *out)
         out[i] = ref_bf16_rne(v[i]);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Gated feed-forward activation feeding the down projection.               */
+/* ------------------------------------------------------------------------ */
+
+/* The model card's configuration table gives the architecture as the Qwen3-1.7B
+ * configuration (feed-forward size 6,144); that configuration's feed-forward
+ * block is the SiLU-gated linear unit (SwiGLU of the GLU-variants paper,
+ * Shazeer 2020, with the Swish parameter fixed at 1):
+ *     h = silu(g) * u,   silu(g) = g * sigmoid(g) = g / (1 + e^-g),
+ * with g the gate projection's output and u the up projection's.  The pages
+ * do not state it; this is the reading taken.  Evaluated in FP64 straight
+ * from the definition (exp(-g) overflows to +inf for g < -709, where the
+ * quotient is the correctly signed zero). */
+double ref_swiglu(double g, double u)
+{
+    return g * u / (1.0 + exp(-g));
+}
+
+void ref_swiglu_array(const double *g, const double *u, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = ref_swiglu(g[i], u[i]);
+}
+
 int ref_num_threads(void)
 {
 #ifdef _OPENMP
