@@ -16,7 +16,10 @@ Puro-2B-Base model card (Qwen3-1.7B configuration: hidden 2,048, FFN 6,144,
 
 Inputs are seeded synthetic tensors already resident in HBM: activations
 BF16 N(0,1), gradients BF16 N(0,1e-3), FP32 master weights N(0,0.02), fresh
-per layer.  Output: one JSON line (see the end of main()).
+per layer.  Output: one JSON line (see the end of main()).  Besides the step,
+the gated activation fused into the dual quantiser (the down projection's
+input formed from the gate/up product) is timed on its own and reported under
+"side_kernels"; it is not part of the step or of its FLOP rate.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -158,6 +161,43 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
         gs = [g for g, _, _, _ in synth.LAYER_GEMMS]
         grouped(NT, S1, F32, [wgrad(g) for g in gs], "gemm_wgrad_NT_1x128_f32", fl(gs))
     return plan, keep
+
+
+def swiglu_side(pf, torch, dev, tokens, sp, reps):
+    """The gated activation fused into the dual quantiser, timed on its own (it is not a
+    quantiser of the step): the down projection's input formed from the two halves of the
+    BF16 [tokens][2 x 6144] gate/up product, h not stored (the step needs only its codes).
+    Algorithmic bytes per element: 2 x 2 read + 2 x 1 written + 2 scales per 128."""
+    import synth
+    F = 6144
+    gu = synth.device_normal((tokens, 2 * F), 1.0, 9001, "bf16", dev)
+    qr = torch.empty((tokens, F), dtype=torch.uint8, device=dev)
+    sr = torch.empty((tokens, F // 128), dtype=torch.float32, device=dev)
+    qt = torch.empty((F, tokens), dtype=torch.uint8, device=dev)
+    st = torch.empty((F, tokens // 128), dtype=torch.float32, device=dev)
+    fn = pf.lib().puro_fp8_swiglu_quant_dual
+    args = (ctypes.c_void_p(gu.data_ptr()), 2 * F, ctypes.c_void_p(gu.data_ptr() + 2 * F), 2 * F, tokens, F,
+            None, 0, ctypes.c_void_p(qr.data_ptr()), F, ctypes.c_void_p(sr.data_ptr()), 1,
+            ctypes.c_void_p(qt.data_ptr()), tokens, ctypes.c_void_p(st.data_ptr()), sp)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        if fn(*args):
+            raise RuntimeError("puro_fp8_swiglu_quant_dual failed")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(reps, 1) * 10
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn(*args)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n
+    nbytes = tokens * F * (4 + 2 + 8 / 128)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log("  swiglu_quant_dual [%d x %d] (outside the step): %.1f us per call, %.0f GB/s"
+        % (tokens, F, us, gbs))
+    return {"shape": [tokens, F], "avg_us": round(us, 2), "bytes": int(nbytes), "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(rows):
@@ -325,6 +365,8 @@ def main():
             k, v[0] / args.steps, v[3] // args.steps, v[0] / v[3] * 1e3,
             ("%.0f TFLOP/s" % (v[1] / v[0] / 1e9)) if v[1] else ("%.0f GB/s" % (v[2] / v[0] / 1e6))))
 
+    side = {"swiglu_quant_dual": swiglu_side(pf, torch, dev, tokens, sp, args.steps)}
+
     dom_name, dom = max(per_name.items(), key=lambda kv: kv[1][0])
     gemm_ms = per_kind["gemm"][0] / args.steps
     if dom[1] > 0:
@@ -361,6 +403,7 @@ def main():
         "gemm_only_tflops": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1),
         "breakdown_ms": {k: round(v[0] / args.steps, 3) for k, v in per_kind.items()},
         "roofline": roofline,
+        "side_kernels": side,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample ...")

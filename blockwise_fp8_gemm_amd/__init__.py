@@ -11,6 +11,7 @@ Names mirror the C entry points:
     puro_fp8_quant_weight_grouped([w..])  -> [(q, s)..] several weights, one launch
     puro_fp8_quant_transpose(x, t_out)    -> (q, s)   128-token blocks per column
     puro_fp8_quant_dual(x, t_out)         -> both of the above from one read of x
+    puro_fp8_swiglu_quant_dual(gate, up)  -> h = bf16(silu(gate) * up) and its dual quantisation
     puro_fp8_gemm(layout, A, sA, B, sB, bgran, out_dtype) -> C
     puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
     puro_status_string(status)
@@ -93,6 +94,10 @@ def lib():
             f = getattr(L, name)
             f.restype = i32
             f.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp, vp]
+        for name in ("puro_fp8_swiglu_quant_dual", "puro_fp8_swiglu_quant_dual_pow2"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, vp, i64, vp, i32, vp, i64, vp, vp]
         L.puro_fp8_gemm_workspace_size.restype = ctypes.c_size_t
         L.puro_fp8_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i32]
         for name in ("puro_fp8_gemm", "puro_fp8_gemm_mx"):
@@ -268,30 +273,61 @@ def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None,
     return q, s
 
 
+def _dual_outs(tokens, cols, transpose_out, device, q_row, s_row, q_tok, s_tok):
+    if q_row is None:
+        q_row = empty_2d(tokens, cols, torch.uint8, device)
+    if s_row is None:
+        s_row = torch.empty((tokens, _nblk(cols)), dtype=torch.float32, device=device)
+    qshape = (cols, tokens) if transpose_out else (tokens, cols)
+    sshape = (cols, _nblk(tokens)) if transpose_out else (_nblk(tokens), cols)
+    if q_tok is None:
+        q_tok = empty_2d(qshape[0], qshape[1], torch.uint8, device)
+    if s_tok is None:
+        s_tok = torch.empty(sshape, dtype=torch.float32, device=device)
+    _need(q_row, (tokens, cols), torch.uint8, "q_row")
+    _need_dense(s_row, (tokens, _nblk(cols)), "s_row")
+    _need(q_tok, qshape, torch.uint8, "q_tok")
+    _need_dense(s_tok, sshape, "s_tok")
+    return q_row, s_row, q_tok, s_tok
+
+
 def puro_fp8_quant_dual(x, transpose_out=True, q_row=None, s_row=None, q_tok=None, s_tok=None,
                         stream=None, pow2=False):
     """One read of x [tokens][cols]: the outputs of puro_fp8_quant_act(x) and of
     puro_fp8_quant_transpose(x, transpose_out).  Returns (q_row, s_row, q_tok, s_tok)."""
     tokens, cols = x.shape
-    if q_row is None:
-        q_row = empty_2d(tokens, cols, torch.uint8, x.device)
-    if s_row is None:
-        s_row = torch.empty((tokens, _nblk(cols)), dtype=torch.float32, device=x.device)
-    qshape = (cols, tokens) if transpose_out else (tokens, cols)
-    sshape = (cols, _nblk(tokens)) if transpose_out else (_nblk(tokens), cols)
-    if q_tok is None:
-        q_tok = empty_2d(qshape[0], qshape[1], torch.uint8, x.device)
-    if s_tok is None:
-        s_tok = torch.empty(sshape, dtype=torch.float32, device=x.device)
-    _need(q_row, (tokens, cols), torch.uint8, "q_row")
-    _need_dense(s_row, (tokens, _nblk(cols)), "s_row")
-    _need(q_tok, qshape, torch.uint8, "q_tok")
-    _need_dense(s_tok, sshape, "s_tok")
+    q_row, s_row, q_tok, s_tok = _dual_outs(tokens, cols, transpose_out, x.device, q_row, s_row, q_tok, s_tok)
     fn = lib().puro_fp8_quant_dual_pow2 if pow2 else lib().puro_fp8_quant_dual
     _check(fn(_ptr(x), _dtype_code(x), tokens, cols, _ld(x), _ptr(q_row), _ld(q_row), _ptr(s_row),
               1 if transpose_out else 0, _ptr(q_tok), _ld(q_tok), _ptr(s_tok), _stream(stream)),
            "puro_fp8_quant_dual")
     return q_row, s_row, q_tok, s_tok
+
+
+def puro_fp8_swiglu_quant_dual(gate, up, transpose_out=True, h=None, store_h=True, q_row=None, s_row=None,
+                               q_tok=None, s_tok=None, stream=None, pow2=False):
+    """h = bf16(silu(gate) * up) for bfloat16 gate, up [tokens][cols], quantised as
+    puro_fp8_quant_dual(h, transpose_out) would.  h is written to `h` (allocated when None)
+    unless store_h is False.  Returns (h or None, q_row, s_row, q_tok, s_tok)."""
+    if gate.shape != up.shape:
+        raise ValueError("gate and up shapes differ: %s vs %s" % (tuple(gate.shape), tuple(up.shape)))
+    if gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
+        raise TypeError("gate and up must be bfloat16")
+    tokens, cols = gate.shape
+    if store_h:
+        if h is None:
+            h = empty_2d(tokens, cols, torch.bfloat16, gate.device)
+        _need(h, (tokens, cols), torch.bfloat16, "h")
+    else:
+        h = None
+    q_row, s_row, q_tok, s_tok = _dual_outs(tokens, cols, transpose_out, gate.device, q_row, s_row, q_tok,
+                                            s_tok)
+    fn = lib().puro_fp8_swiglu_quant_dual_pow2 if pow2 else lib().puro_fp8_swiglu_quant_dual
+    _check(fn(_ptr(gate), _ld(gate), _ptr(up), _ld(up), tokens, cols,
+              _ptr(h) if h is not None else ctypes.c_void_p(0), _ld(h) if h is not None else 0,
+              _ptr(q_row), _ld(q_row), _ptr(s_row), 1 if transpose_out else 0, _ptr(q_tok), _ld(q_tok),
+              _ptr(s_tok), _stream(stream)), "puro_fp8_swiglu_quant_dual")
+    return h, q_row, s_row, q_tok, s_tok
 
 
 def gemm_dims(layout, A, B):

@@ -159,7 +159,57 @@ static puro_status_t quant_dual_impl(const void *x, puro_dtype_t xdt, int64_t to
     }
 }
 
+static puro_status_t swiglu_dual_impl(const void *gate, int64_t ldg, const void *up, int64_t ldu,
+                                      int64_t tokens, int64_t cols, void *h, int64_t ldh, uint8_t *q_row,
+                                      int64_t ldq_row, float *s_row, int transpose_out, uint8_t *q_tok,
+                                      int64_t ldq_tok, float *s_tok, bool pow2, hipStream_t stream)
+{
+    try {
+        if (transpose_out != 0 && transpose_out != 1)
+            return PURO_ERR_ENUM;
+        puro_status_t st = check_quant(gate, PURO_BF16, tokens, cols, ldg, q_row, ldq_row, cols, s_row);
+        if (st != PURO_OK)
+            return st;
+        st = check_quant(up, PURO_BF16, tokens, cols, ldu, q_tok, ldq_tok, transpose_out ? tokens : cols,
+                         s_tok);
+        if (st != PURO_OK)
+            return st;
+        if (h) {
+            if (bad_ld(ldh, cols))
+                return PURO_ERR_SHAPE;
+            if (ldh % 16 || !aligned(h, 16))
+                return PURO_ERR_ALIGN;
+        }
+        if (tokens == 0 || cols == 0)
+            return PURO_OK;
+        return from_hip(puro::launch_swiglu_dual(static_cast<const uint16_t *>(gate), ldg,
+                                                 static_cast<const uint16_t *>(up), ldu,
+                                                 static_cast<uint16_t *>(h), ldh, tokens, cols, q_row, ldq_row,
+                                                 s_row, transpose_out == 1, q_tok, ldq_tok, s_tok, pow2, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
 extern "C" {
+
+puro_status_t puro_fp8_swiglu_quant_dual(const void *gate, int64_t ldg, const void *up, int64_t ldu,
+                                         int64_t tokens, int64_t cols, void *h, int64_t ldh, uint8_t *q_row,
+                                         int64_t ldq_row, float *s_row, int transpose_out, uint8_t *q_tok,
+                                         int64_t ldq_tok, float *s_tok, hipStream_t stream)
+{
+    return swiglu_dual_impl(gate, ldg, up, ldu, tokens, cols, h, ldh, q_row, ldq_row, s_row, transpose_out,
+                            q_tok, ldq_tok, s_tok, false, stream);
+}
+
+puro_status_t puro_fp8_swiglu_quant_dual_pow2(const void *gate, int64_t ldg, const void *up, int64_t ldu,
+                                              int64_t tokens, int64_t cols, void *h, int64_t ldh,
+                                              uint8_t *q_row, int64_t ldq_row, float *s_row, int transpose_out,
+                                              uint8_t *q_tok, int64_t ldq_tok, float *s_tok, hipStream_t stream)
+{
+    return swiglu_dual_impl(gate, ldg, up, ldu, tokens, cols, h, ldh, q_row, ldq_row, s_row, transpose_out,
+                            q_tok, ldq_tok, s_tok, true, stream);
+}
 
 puro_status_t puro_fp8_quant_act(const void *x, puro_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t *q, int64_t ldq, float *s, hipStream_t stream)

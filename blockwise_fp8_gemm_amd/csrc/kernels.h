@@ -34,6 +34,13 @@ hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t c
                              uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
                              int64_t ldqt, float *st, bool pow2, hipStream_t stream);
 
+// Dual quantiser of h = BF16(silu(g) * u), g and u BF16 [tokens][cols]; h is
+// also stored unless NULL.
+hipError_t launch_swiglu_dual(const uint16_t *g, int64_t ldg, const uint16_t *u, int64_t ldu, uint16_t *h,
+                              int64_t ldh, int64_t tokens, int64_t cols, uint8_t *qr, int64_t ldqr, float *sr,
+                              bool transpose_out, uint8_t *qt, int64_t ldqt, float *st, bool pow2,
+                              hipStream_t stream);
+
 constexpr int kGemmMaxSeg = 4;
 
 // One K segment of a product: A, B and their block scales over K indices 0 .. K-1.

@@ -322,14 +322,39 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const T *__restric
 // input, the untransposed token-block copy and the ragged edge tiles of the
 // packed BF16 kernel below; (bx0, by0) offsets the tile grid for the latter.
 // ---------------------------------------------------------------------------
-template <typename T, bool TRANSPOSE_OUT>
+__device__ __forceinline__ float lo16f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi16f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// SiLU-gated activation h = silu(g) * u, silu(g) = g / (1 + e^-g), in FP32 for
+// BF16 g and u (the feed-forward block of the Qwen3-1.7B configuration the
+// model card names).  g * u is exact (two 8-bit significands).  e = exp(-|g|)
+// lies in (0, 1]: sigmoid(g) = 1 / (1 + e) for g >= 0 and e / (1 + e) for
+// g < 0, so nothing overflows.  Relative error: a few FP32 ulps (expf, the
+// reciprocal, two products); where e is subnormal (g < -87.3) its absolute
+// error 2^-149 carries over as 2^-149 |g u|.
+__device__ __forceinline__ float swiglu_f32(float g, float u)
+{
+    const float e = expf(-fabsf(g));
+    const float sig = (g < 0.0f ? e : 1.0f) * __builtin_amdgcn_rcpf(1.0f + e);
+    return (g * u) * sig;
+}
+
+// Two packed BF16 gate values and two up values -> two packed BF16 activations.
+__device__ __forceinline__ uint32_t swiglu2(uint32_t g2, uint32_t u2)
+{
+    return to_bf16x2(swiglu_f32(lo16f(g2), lo16f(u2)), swiglu_f32(hi16f(g2), hi16f(u2)));
+}
+
+template <typename T, bool TRANSPOSE_OUT, bool SWIGLU>
 __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x, int64_t tokens,
                                                          int64_t cols, int64_t ldx,
                                                          uint8_t *__restrict__ qr, int64_t ldqr,
                                                          float *__restrict__ sr, int64_t nbr,
                                                          uint8_t *__restrict__ qt, int64_t ldqt,
                                                          float *__restrict__ st, int64_t ntb, int pow2,
-                                                         int bx0, int by0)
+                                                         int bx0, int by0,
+                                                         const uint16_t *__restrict__ up, int64_t ldu,
+                                                         uint16_t *__restrict__ hout, int64_t ldh)
 {
     __shared__ float red[4][128];
     __shared__ float scl[128];
@@ -348,7 +373,34 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const T *__restrict__ x
     for (int i = 0; i < 8; i++) {
         const int64_t tk = tok0 + 8 * rq + i;
         const T *xr = x + tk * ldx;
-        if (full) {
+        if constexpr (SWIGLU) {
+            // x is the gate, up the up projection; h = BF16(silu(gate) * up)
+            const uint16_t *ur = up + tk * ldu;
+            if (full) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(xr + c0);
+                const uint4 b = *reinterpret_cast<const uint4 *>(ur + c0);
+                const uint32_t hv[4] = {swiglu2(a.x, b.x), swiglu2(a.y, b.y), swiglu2(a.z, b.z),
+                                        swiglu2(a.w, b.w)};
+                if (hout)
+                    *reinterpret_cast<uint4 *>(hout + tk * ldh + c0) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+#pragma unroll
+                for (int p = 0; p < 4; p++) {
+                    v[i][2 * p] = lo16f(hv[p]);
+                    v[i][2 * p + 1] = hi16f(hv[p]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    v[i][j] = 0.0f;
+                    if (tk < tokens && c0 + j < cols) {
+                        const uint32_t hb = swiglu2(xr[c0 + j], ur[c0 + j]) & 0xFFFFu;
+                        if (hout)
+                            hout[tk * ldh + c0 + j] = (uint16_t)hb;
+                        v[i][j] = lo16f(hb);
+                    }
+                }
+            }
+        } else if (full) {
             Elem<T>::load8(xr + c0, v[i]);
         } else {
 #pragma unroll
@@ -536,9 +588,6 @@ __device__ __forceinline__ uint32_t q4(float a, float b, float c, float d, float
     return e4m3x4(qdiv<SLOW>(a, s, r), qdiv<SLOW>(b, s, r), qdiv<SLOW>(c, s, r), qdiv<SLOW>(d, s, r));
 }
 
-__device__ __forceinline__ float lo16f(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi16f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
-
 // Quantise this thread's 8 tokens x 8 columns both ways: row codes straight to
 // global memory, token-block codes into the LDS tile.
 template <bool SLOW>
@@ -579,35 +628,66 @@ __device__ __forceinline__ void dual_bf16_quant(uint32_t (&raw)[8][4], const flo
     }
 }
 
-__device__ __forceinline__ void dual_bf16_load(uint32_t (&raw)[8][4], const uint16_t *x_t, int ldx,
-                                               int rq, int cc)
-{
+// Where a tile's BF16 values come from: read from x (DualPlain), or formed
+// from the gate and up projections' outputs and optionally stored (DualSwiglu).
+// at() moves a source to a tile's first element; in-tile offsets fit 32 bits.
+struct DualPlain {
+    const uint16_t *x;
+    int ldx;
+    __device__ __forceinline__ DualPlain at(int64_t t0, int64_t c0) const { return {x + t0 * ldx + c0, ldx}; }
+    __device__ __forceinline__ void load(uint32_t (&raw)[8][4], int rq, int cc) const
+    {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(x_t + (8 * rq + i) * ldx + cc * 8);
-        raw[i][0] = a.x; raw[i][1] = a.y; raw[i][2] = a.z; raw[i][3] = a.w;
+        for (int i = 0; i < 8; i++) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(x + (8 * rq + i) * ldx + cc * 8);
+            raw[i][0] = a.x; raw[i][1] = a.y; raw[i][2] = a.z; raw[i][3] = a.w;
+        }
     }
-}
+};
+
+struct DualSwiglu {
+    const uint16_t *g, *u;
+    uint16_t *h;   // NULL: the activation is not stored
+    int ldg, ldu, ldh;
+    __device__ __forceinline__ DualSwiglu at(int64_t t0, int64_t c0) const
+    {
+        return {g + t0 * ldg + c0, u + t0 * ldu + c0, h ? h + t0 * ldh + c0 : nullptr, ldg, ldu, ldh};
+    }
+    __device__ __forceinline__ void load(uint32_t (&raw)[8][4], int rq, int cc) const
+    {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int r = 8 * rq + i;
+            const uint4 a = *reinterpret_cast<const uint4 *>(g + r * ldg + cc * 8);
+            const uint4 b = *reinterpret_cast<const uint4 *>(u + r * ldu + cc * 8);
+            raw[i][0] = swiglu2(a.x, b.x);
+            raw[i][1] = swiglu2(a.y, b.y);
+            raw[i][2] = swiglu2(a.z, b.z);
+            raw[i][3] = swiglu2(a.w, b.w);
+            if (h)
+                *reinterpret_cast<uint4 *>(h + r * ldh + cc * 8) = make_uint4(raw[i][0], raw[i][1], raw[i][2], raw[i][3]);
+        }
+    }
+};
 
 // Tiles holding a block whose scale is below 2^-80 (never in practice): reload
 // the values and divide those blocks exactly, outside the fast kernel body.
-__device__ __attribute__((noinline)) void dual_bf16_slow(const uint16_t *x_t, int ldx,
-                                                         const float2 *rsc, const float *scl,
+template <class Src>
+__device__ __attribute__((noinline)) void dual_bf16_slow(const Src src, const float2 *rsc, const float *scl,
                                                          const float *rcl, uint32_t (*tile)[33],
                                                          uint8_t *qr_t, int ldqr, int rq, int cc)
 {
     uint32_t raw[8][4];
-    dual_bf16_load(raw, x_t, ldx, rq, cc);
+    src.load(raw, rq, cc);
     dual_bf16_quant<true>(raw, rsc, scl, rcl, tile, qr_t, ldqr, rq, cc);
 }
 
-// Full 128 x 128 tiles only (the launcher sends ragged edge tiles to
+// One full 128 x 128 tile (the launcher sends ragged edge tiles to
 // quant_dual_kernel); offsets inside a tile fit 32 bits (checked by the launcher).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
-void quant_dual_bf16_kernel(const uint16_t *__restrict__ x, int ldx, uint8_t *__restrict__ qr,
-                            int ldqr, float *__restrict__ sr, int64_t nbr,
-                            uint8_t *__restrict__ qt, int ldqt, float *__restrict__ st,
-                            int64_t ntb, int pow2)
+template <class Src>
+__device__ __forceinline__ void dual_bf16_tile(const Src &src, uint8_t *__restrict__ qr, int ldqr,
+                                               float *__restrict__ sr, int64_t nbr, uint8_t *__restrict__ qt,
+                                               int ldqt, float *__restrict__ st, int64_t ntb, int pow2)
 {
     __shared__ uint32_t red[4][64];           // [wave][column pair] packed column maxima
     __shared__ float scl[128], rcl[128];       // column scales and reciprocals
@@ -618,10 +698,10 @@ void quant_dual_bf16_kernel(const uint16_t *__restrict__ x, int ldx, uint8_t *__
     const int cc = t & 15, rq = t >> 4, l16 = t & 15;
     const int64_t tok0 = (int64_t)blockIdx.y * 128;
     const int64_t col0 = (int64_t)blockIdx.x * 128;
-    const uint16_t *x_t = x + tok0 * ldx + col0;
+    const Src src_t = src.at(tok0, col0);
 
     uint32_t raw[8][4];
-    dual_bf16_load(raw, x_t, ldx, rq, cc);
+    src_t.load(raw, rq, cc);
     constexpr uint32_t MAG = 0x7FFF7FFFu;
 
     // ---- column partial maxima over this thread's 8 tokens, then the wave's 4 rows
@@ -672,7 +752,7 @@ void quant_dual_bf16_kernel(const uint16_t *__restrict__ x, int ldx, uint8_t *__
     }
     uint8_t *qr_t = qr + tok0 * ldqr + col0;
     if (__syncthreads_or(slow))
-        dual_bf16_slow(x_t, ldx, rsc, scl, rcl, tile, qr_t, ldqr, rq, cc);
+        dual_bf16_slow(src_t, rsc, scl, rcl, tile, qr_t, ldqr, rq, cc);
     else
         dual_bf16_quant<false>(raw, rsc, scl, rcl, tile, qr_t, ldqr, rq, cc);
     __syncthreads();
@@ -684,6 +764,27 @@ void quant_dual_bf16_kernel(const uint16_t *__restrict__ x, int ldx, uint8_t *__
         const uint32_t *src = &tile[row][seg * 4];
         *reinterpret_cast<uint4 *>(qt_t + row * ldqt + seg * 16) = make_uint4(src[0], src[1], src[2], src[3]);
     }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
+void quant_dual_bf16_kernel(const uint16_t *__restrict__ x, int ldx, uint8_t *__restrict__ qr,
+                            int ldqr, float *__restrict__ sr, int64_t nbr,
+                            uint8_t *__restrict__ qt, int ldqt, float *__restrict__ st,
+                            int64_t ntb, int pow2)
+{
+    dual_bf16_tile(DualPlain{x, ldx}, qr, ldqr, sr, nbr, qt, ldqt, st, ntb, pow2);
+}
+
+// The same with the tile's values formed as silu(gate) * up (and stored to h
+// unless h is NULL).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void swiglu_dual_bf16_kernel(const uint16_t *__restrict__ g, int ldg, const uint16_t *__restrict__ u,
+                             int ldu, uint16_t *__restrict__ h, int ldh, uint8_t *__restrict__ qr,
+                             int ldqr, float *__restrict__ sr, int64_t nbr,
+                             uint8_t *__restrict__ qt, int ldqt, float *__restrict__ st,
+                             int64_t ntb, int pow2)
+{
+    dual_bf16_tile(DualSwiglu{g, u, h, ldg, ldu, ldh}, qr, ldqr, sr, nbr, qt, ldqt, st, ntb, pow2);
 }
 
 // ---------------------------------------------------------------------------
@@ -777,9 +878,17 @@ hipError_t launch_quant_transpose(const void *x, bool bf16, int64_t tokens, int6
     return hipGetLastError();
 }
 
-hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t cols, int64_t ldx,
-                             uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
-                             int64_t ldqt, float *st, bool pow2, hipStream_t stream)
+// The gate's partner and the activation output of the fused SwiGLU variant.
+struct SwigluIn {
+    const uint16_t *u;
+    int64_t ldu;
+    uint16_t *h;
+    int64_t ldh;
+};
+
+static hipError_t dual_launch(const void *x, bool bf16, int64_t tokens, int64_t cols, int64_t ldx,
+                              uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
+                              int64_t ldqt, float *st, bool pow2, const SwigluIn *sw, hipStream_t stream)
 {
     const int64_t ntb = (tokens + 127) / 128, ncb = (cols + 127) / 128;
     if (ntb == 0 || ncb == 0)
@@ -788,32 +897,47 @@ hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t c
     // (in-tile offsets of at most 127 leading dimensions must fit 32 bits)
     int64_t fb_x = 0, fb_y = 0;
     const int64_t lim = ((int64_t)1 << 31) / 256;
-    if (bf16 && transpose_out && ldx < lim && ldqr < lim && ldqt < lim) {
+    const bool sw_ld_ok = !sw || (sw->ldu < lim && sw->ldh < lim);
+    if (bf16 && transpose_out && ldx < lim && ldqr < lim && ldqt < lim && sw_ld_ok) {
         fb_x = cols / 128;
         fb_y = tokens / 128;
-        if (fb_x > 0 && fb_y > 0)
-            hipLaunchKernelGGL(quant_dual_bf16_kernel, dim3((unsigned)fb_x, (unsigned)fb_y), dim3(256), 0,
-                               stream, (const uint16_t *)x, (int)ldx, qr, (int)ldqr, sr, ncb, qt, (int)ldqt,
-                               st, ntb, (int)pow2);
-        else
+        if (fb_x > 0 && fb_y > 0) {
+            const dim3 grid((unsigned)fb_x, (unsigned)fb_y);
+            if (sw)
+                hipLaunchKernelGGL(swiglu_dual_bf16_kernel, grid, dim3(256), 0, stream, (const uint16_t *)x,
+                                   (int)ldx, sw->u, (int)sw->ldu, sw->h, (int)sw->ldh, qr, (int)ldqr, sr, ncb,
+                                   qt, (int)ldqt, st, ntb, (int)pow2);
+            else
+                hipLaunchKernelGGL(quant_dual_bf16_kernel, grid, dim3(256), 0, stream, (const uint16_t *)x,
+                                   (int)ldx, qr, (int)ldqr, sr, ncb, qt, (int)ldqt, st, ntb, (int)pow2);
+        } else {
             fb_x = fb_y = 0;
+        }
     }
     // the rest: tiles right of the full columns (all token tiles), then the tiles
     // below the full rows (full columns only)
+    const uint16_t *u = sw ? sw->u : nullptr;
+    uint16_t *h = sw ? sw->h : nullptr;
+    const int64_t ldu = sw ? sw->ldu : 0, ldh = sw ? sw->ldh : 0;
     auto rest = [&](dim3 grid, int bx0, int by0) {
-#define PURO_DUAL(T, TR)                                                                            \
-    hipLaunchKernelGGL((quant_dual_kernel<T, TR>), grid, dim3(256), 0, stream, (const T *)x, tokens, \
-                       cols, ldx, qr, ldqr, sr, ncb, qt, ldqt, st, ntb, (int)pow2, bx0, by0)
-        if (bf16) {
+#define PURO_DUAL(T, TR, SW)                                                                          \
+    hipLaunchKernelGGL((quant_dual_kernel<T, TR, SW>), grid, dim3(256), 0, stream, (const T *)x, tokens, \
+                       cols, ldx, qr, ldqr, sr, ncb, qt, ldqt, st, ntb, (int)pow2, bx0, by0, u, ldu, h, ldh)
+        if (sw) {
             if (transpose_out)
-                PURO_DUAL(uint16_t, true);
+                PURO_DUAL(uint16_t, true, true);
             else
-                PURO_DUAL(uint16_t, false);
+                PURO_DUAL(uint16_t, false, true);
+        } else if (bf16) {
+            if (transpose_out)
+                PURO_DUAL(uint16_t, true, false);
+            else
+                PURO_DUAL(uint16_t, false, false);
         } else {
             if (transpose_out)
-                PURO_DUAL(float, true);
+                PURO_DUAL(float, true, false);
             else
-                PURO_DUAL(float, false);
+                PURO_DUAL(float, false, false);
         }
 #undef PURO_DUAL
     };
@@ -826,6 +950,24 @@ hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t c
             rest(dim3((unsigned)fb_x, (unsigned)(ntb - fb_y)), 0, (int)fb_y);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const void *x, bool bf16, int64_t tokens, int64_t cols, int64_t ldx,
+                             uint8_t *qr, int64_t ldqr, float *sr, bool transpose_out, uint8_t *qt,
+                             int64_t ldqt, float *st, bool pow2, hipStream_t stream)
+{
+    return dual_launch(x, bf16, tokens, cols, ldx, qr, ldqr, sr, transpose_out, qt, ldqt, st, pow2, nullptr,
+                       stream);
+}
+
+hipError_t launch_swiglu_dual(const uint16_t *g, int64_t ldg, const uint16_t *u, int64_t ldu, uint16_t *h,
+                              int64_t ldh, int64_t tokens, int64_t cols, uint8_t *qr, int64_t ldqr, float *sr,
+                              bool transpose_out, uint8_t *qt, int64_t ldqt, float *st, bool pow2,
+                              hipStream_t stream)
+{
+    const SwigluIn sw{u, ldu, h, ldh};
+    return dual_launch(g, true, tokens, cols, ldg, qr, ldqr, sr, transpose_out, qt, ldqt, st, pow2, &sw,
+                       stream);
 }
 
 } // namespace puro

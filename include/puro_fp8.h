@@ -154,6 +154,30 @@ puro_status_t puro_fp8_quant_dual(const void *x, puro_dtype_t xdt, int64_t token
                                   hipStream_t stream);
 
 /*
+ * Gated activation fused into the dual quantiser: the down projection's input.
+ * The model card's configuration table names the Qwen3-1.7B configuration,
+ * whose feed-forward block multiplies the up projection's output by SiLU of
+ * the gate projection's (SwiGLU with Swish parameter 1; the pages do not state
+ * the activation, this is the reading taken).  For g = gate[t][c] and
+ * u = up[t][c] (BF16, [tokens][cols], strides ldg and ldu; the two may be the
+ * halves of one [tokens][2 cols] product):
+ *     h[t][c] = BF16_RNE( silu(g) * u ),   silu(g) = g / (1 + e^-g).
+ * silu(g) * u is evaluated in FP32 before the one BF16 rounding, within
+ * 2^-20 |silu(g) u| + 2^-149 (|g u| + 1) of the exact value (the second term
+ * only matters where sigmoid(g) is below FP32's normal range, g < -87.3).
+ * h is stored (BF16 [tokens][cols], stride ldh) unless h is NULL.  Either way
+ * q_row/s_row and q_tok/s_tok are exactly what puro_fp8_quant_dual writes for
+ * that h tensor with the same transpose_out.  |g u| must be finite in FP32.
+ * Every output must be disjoint from gate and up and from each other.
+ * Errors as puro_fp8_quant_dual; when h is not NULL, ldh is checked like any
+ * leading dimension and h must be 16-byte aligned.
+ */
+puro_status_t puro_fp8_swiglu_quant_dual(const void *gate, int64_t ldg, const void *up, int64_t ldu,
+                                         int64_t tokens, int64_t cols, void *h, int64_t ldh, uint8_t *q_row,
+                                         int64_t ldq_row, float *s_row, int transpose_out, uint8_t *q_tok,
+                                         int64_t ldq_tok, float *s_tok, hipStream_t stream);
+
+/*
  * Workspace bytes puro_fp8_gemm needs for this problem (0 = none).  Returns 0
  * for invalid arguments as well; puro_fp8_gemm reports those.
  */
@@ -268,6 +292,10 @@ puro_status_t puro_fp8_quant_dual_pow2(const void *x, puro_dtype_t xdt, int64_t 
                                        int64_t ldx, uint8_t *q_row, int64_t ldq_row, float *s_row,
                                        int transpose_out, uint8_t *q_tok, int64_t ldq_tok, float *s_tok,
                                        hipStream_t stream);
+puro_status_t puro_fp8_swiglu_quant_dual_pow2(const void *gate, int64_t ldg, const void *up, int64_t ldu,
+                                              int64_t tokens, int64_t cols, void *h, int64_t ldh,
+                                              uint8_t *q_row, int64_t ldq_row, float *s_row, int transpose_out,
+                                              uint8_t *q_tok, int64_t ldq_tok, float *s_tok, hipStream_t stream);
 
 /*
  * GEMM on the scaled FP8 matrix cores: arguments, storage and result

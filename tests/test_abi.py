@@ -35,6 +35,7 @@ def test_header_declares_the_calls():
               "puro_fp8_quant_transpose_pow2", "puro_fp8_quant_dual_pow2", "puro_fp8_gemm_mx",
               "puro_fp8_gemm_mx_workspace_size", "puro_status_string",
               "puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2",
+              "puro_fp8_swiglu_quant_dual", "puro_fp8_swiglu_quant_dual_pow2",
               "puro_fp8_version"):
         assert n in names
 
@@ -126,6 +127,33 @@ def test_quant_dual_validation():
     assert _qd(ldqr=136) == ALIGN
     assert _qd(qt=P_ODD) == ALIGN
     assert _qd(x=NUL, qr=NUL, sr=NUL, qt=NUL, st=NUL, tokens=0, ldqt=0) == OK
+
+
+def _sw(g=P, ldg=128, u=P, ldu=128, tokens=256, cols=128, h=P, ldh=128, qr=P, ldqr=128, sr=P, t=1, qt=P,
+        ldqt=256, st=P, pow2=False):
+    L = pf.lib()
+    fn = L.puro_fp8_swiglu_quant_dual_pow2 if pow2 else L.puro_fp8_swiglu_quant_dual
+    return fn(g, ldg, u, ldu, tokens, cols, h, ldh, qr, ldqr, sr, t, qt, ldqt, st, None)
+
+
+def test_swiglu_quant_dual_validation():
+    for pow2 in (False, True):
+        assert _sw(t=2, pow2=pow2) == ENUM
+        assert _sw(ldg=64, pow2=pow2) == SHAPE       # gate rows hold `cols` values
+        assert _sw(ldu=64, pow2=pow2) == SHAPE
+        assert _sw(ldh=64, pow2=pow2) == SHAPE
+        assert _sw(ldqt=128, pow2=pow2) == SHAPE     # transposed copy rows hold `tokens` codes
+        assert _sw(cols=-1, pow2=pow2) == SHAPE
+        assert _sw(g=NUL, pow2=pow2) == NULL
+        assert _sw(u=NUL, pow2=pow2) == NULL
+        assert _sw(sr=NUL, pow2=pow2) == NULL
+        assert _sw(ldu=136, pow2=pow2) == ALIGN
+        assert _sw(ldh=136, pow2=pow2) == ALIGN
+        assert _sw(h=P_ODD, pow2=pow2) == ALIGN
+        assert _sw(u=P_ODD, pow2=pow2) == ALIGN
+        # h is optional: NULL h with any ldh is valid; empty problems enqueue nothing
+        assert _sw(g=NUL, u=NUL, h=NUL, ldh=0, qr=NUL, sr=NUL, qt=NUL, st=NUL, tokens=0, ldqt=0,
+                   pow2=pow2) == OK
 
 
 def _gemm(layout=0, M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, bg=1, C=P,
