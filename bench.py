@@ -163,10 +163,10 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     return plan, keep
 
 
-def swiglu_side(pf, torch, dev, tokens, sp, reps):
-    """The gated activation fused into the dual quantiser, timed on its own (it is not a
-    quantiser of the step): the down projection's input formed from the two halves of the
-    BF16 [tokens][2 x 6144] gate/up product, h not stored (the step needs only its codes).
+def swiglu_setup(pf, torch, dev, tokens, sp):
+    """The gated activation fused into the dual quantiser at the down projection's input: h formed
+    from the two halves of a resident BF16 [tokens][2 x 6144] gate/up product, not stored (a step
+    needs only its codes).  Returns (fn, args, algorithmic bytes, buffers to keep alive).
     Algorithmic bytes per element: 2 x 2 read + 2 x 1 written + 2 scales per 128."""
     import synth
     F = 6144
@@ -179,6 +179,12 @@ def swiglu_side(pf, torch, dev, tokens, sp, reps):
     args = (ctypes.c_void_p(gu.data_ptr()), 2 * F, ctypes.c_void_p(gu.data_ptr() + 2 * F), 2 * F, tokens, F,
             None, 0, ctypes.c_void_p(qr.data_ptr()), F, ctypes.c_void_p(sr.data_ptr()), 1,
             ctypes.c_void_p(qt.data_ptr()), tokens, ctypes.c_void_p(st.data_ptr()), sp)
+    return fn, args, tokens * F * (4 + 2 + 8 / 128), (gu, qr, sr, qt, st)
+
+
+def swiglu_side(pf, torch, dev, tokens, sp, reps):
+    """swiglu_setup's launch timed on its own (it is not a quantiser of the step)."""
+    fn, args, nbytes, keep = swiglu_setup(pf, torch, dev, tokens, sp)
     stream = torch.cuda.current_stream()
     for _ in range(3):
         if fn(*args):
@@ -192,11 +198,10 @@ def swiglu_side(pf, torch, dev, tokens, sp, reps):
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / n
-    nbytes = tokens * F * (4 + 2 + 8 / 128)
     gbs = nbytes / (us * 1e-6) / 1e9
     log("  swiglu_quant_dual [%d x %d] (outside the step): %.1f us per call, %.0f GB/s"
-        % (tokens, F, us, gbs))
-    return {"shape": [tokens, F], "avg_us": round(us, 2), "bytes": int(nbytes), "GB/s": round(gbs, 1),
+        % (tokens, args[5], us, gbs))
+    return {"shape": [tokens, args[5]], "avg_us": round(us, 2), "bytes": int(nbytes), "GB/s": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
@@ -265,8 +270,9 @@ def measured_traffic(name):
 
 
 def traffic_probe():
-    """One layer of the step, three times, then a plain 1 GiB copy three times
-    (the calibration for the memory counters); run under rocprofv3 --pmc."""
+    """One layer of the step, three times, the fused activation + dual quantiser three times, then
+    a plain 1 GiB copy three times (the calibration for the memory counters); run under
+    rocprofv3 --pmc."""
     import torch
     import blockwise_fp8_gemm_amd as pf
     dev = torch.device("cuda:0")
@@ -276,12 +282,17 @@ def traffic_probe():
     plan, keep = build_stack_plan(pf, torch, dev, 1, synth.TOKENS, sp)
     for _ in range(3):
         plan.run()
+    fn, args, _, keep_sw = swiglu_setup(pf, torch, dev, synth.TOKENS, sp)
+    for _ in range(3):
+        if fn(*args):
+            raise RuntimeError("puro_fp8_swiglu_quant_dual failed")
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print("traffic probe done: 1 layer x 3, then copy of %d bytes x 3" % src.numel(), flush=True)
+    print("traffic probe done: 1 layer x 3, the fused activation x 3, then copy of %d bytes x 3"
+          % src.numel(), flush=True)
 
 
 def main():
