@@ -205,6 +205,145 @@ def swiglu_side(pf, torch, dev, tokens, sp, reps):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def config_runs(pf, torch, dev, sp):
+    """The per-layer configurations of the workload table as lists of single C-ABI calls.
+
+    1 single fwd   X [256,512], W [256,512] FP32 N(0,1): quant_act, quant_weight, gemm NT (FP32 out)
+    2 layer fwd    the fused four-GEMM layer (qkv, o, gate_up, down) at 8,192 tokens: quant_act of
+                   X_g (BF16 N(0,1)), quant_weight of W_g (FP32 N(0,0.02)), gemm NT (BF16 out)
+    3 layer bwd    dY_g BF16 N(0,1e-3): dual quantiser of dY_g (1x128 copy + 128-token copy),
+                   quant_transpose of X_g, gemm NN (dX, BF16) and gemm NT (dW, FP32, K = 8,192);
+                   W_g as quantised by config 2
+    5 outlier      X [16384,6144] BF16 with 1% of channels x100, dY [16384,2048] BF16 lognormal
+                   (exp N(ln 1e-6, 2)), both with 1% zero row and column segments, W [2048,6144]:
+                   dual quantisers of X and dY, quant_weight, fwd NT, dgrad NN, wgrad NT
+    Returns [(name, [(fn, args)], flops, buffers to keep alive)]."""
+    import synth
+    L = pf.lib()
+    vp = ctypes.c_void_p
+    bf16, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+    BF16, F32 = pf.PURO_BF16, pf.PURO_F32
+    NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
+    S1, S128 = pf.BGRAN["1x128"], pf.BGRAN["128x128"]
+
+    def P(t):
+        return vp(t.data_ptr())
+
+    def nb(n):
+        return (n + 127) // 128
+
+    def E(shape, dt):
+        return torch.empty(shape, dtype=dt, device=dev)
+
+    def gemm(layout, M, N, K, A, lda, sA, B, ldb, sB, bg, C, cdt, ldc, keep):
+        ws_n = L.puro_fp8_gemm_workspace_size(layout, M, N, K, bg)
+        ws = E((max(ws_n, 1),), u8)
+        keep.append(ws)
+        return (L.puro_fp8_gemm, (layout, M, N, K, P(A), lda, P(sA), P(B), ldb, P(sB), bg, P(C), cdt, ldc,
+                                  P(ws), ws_n, sp))
+
+    def qweight(w, n, k, q, s):
+        return (L.puro_fp8_quant_weight, (P(w), F32, n, k, k, P(q), k, P(s), sp))
+
+    def qdual(x, t, c, q, s, qt, st):
+        return (L.puro_fp8_quant_dual, (P(x), BF16, t, c, c, P(q), c, P(s), 1, P(qt), t, P(st), sp))
+
+    runs = []
+    # config 1
+    keep = []
+    X = synth.device_normal((256, 512), 1.0, synth.seed_of(1, 0, 0), "f32", dev)
+    W = synth.device_normal((256, 512), 1.0, synth.seed_of(1, 0, 1), "f32", dev)
+    qx, sx, qw, sw, C = E((256, 512), u8), E((256, 4), f32), E((256, 512), u8), E((2, 4), f32), E((256, 256), f32)
+    keep += [X, W, qx, sx, qw, sw, C]
+    calls = [(L.puro_fp8_quant_act, (P(X), F32, 256, 512, 512, P(qx), 512, P(sx), sp)),
+             qweight(W, 256, 512, qw, sw),
+             gemm(NT, 256, 256, 512, qx, 512, sx, qw, 512, sw, S128, C, F32, 256, keep)]
+    runs.append(("1_single_fwd", calls, 2.0 * 256 * 256 * 512, keep))
+
+    # configs 2 and 3
+    T = synth.TOKENS
+    keep2, keep3, c2, c3, fl = [], [], [], [], 0.0
+    for i, (g, n, k) in enumerate(synth.FUSED_GEMMS):
+        X = synth.device_normal((T, k), 1.0, synth.seed_of(2, 0, i), "bf16", dev)
+        W = synth.device_normal((n, k), 0.02, synth.seed_of(2, 0, 10 + i), "f32", dev)
+        dY = synth.device_normal((T, n), 1e-3, synth.seed_of(3, 0, 20 + i), "bf16", dev)
+        qx, sx = E((T, k), u8), E((T, nb(k)), f32)
+        qxt, sxt = E((k, T), u8), E((k, nb(T)), f32)
+        qw, sw = E((n, k), u8), E((nb(n), nb(k)), f32)
+        Y = E((T, n), bf16)
+        qdy, sdy, qdyt, sdyt = E((T, n), u8), E((T, nb(n)), f32), E((n, T), u8), E((n, nb(T)), f32)
+        dX, dW = E((T, k), bf16), E((n, k), f32)
+        keep2 += [X, W, qx, sx, qw, sw, Y]
+        keep3 += [X, dY, qxt, sxt, qdy, sdy, qdyt, sdyt, dX, dW]
+        c2 += [(L.puro_fp8_quant_act, (P(X), BF16, T, k, k, P(qx), k, P(sx), sp)),
+               qweight(W, n, k, qw, sw),
+               gemm(NT, T, n, k, qx, k, sx, qw, k, sw, S128, Y, BF16, n, keep2)]
+        c3 += [qdual(dY, T, n, qdy, sdy, qdyt, sdyt),
+               (L.puro_fp8_quant_transpose, (P(X), BF16, T, k, k, 1, P(qxt), T, P(sxt), sp)),
+               gemm(NN, T, k, n, qdy, n, sdy, qw, k, sw, S128, dX, BF16, k, keep3),
+               gemm(NT, n, k, T, qdyt, T, sdyt, qxt, T, sxt, S1, dW, F32, k, keep3)]
+        fl += 2.0 * T * n * k
+    runs.append(("2_layer_fwd", c2, fl, keep2))
+    runs.append(("3_layer_bwd", c3, 2 * fl, keep3 + keep2))
+
+    # config 5
+    T5, N5, K5 = 16384, 2048, 6144
+    X = synth.device_outlier_activations(T5, K5, synth.seed_of(5, 0, 0), dev)
+    dY = synth.device_lognormal_gradients(T5, N5, synth.seed_of(5, 0, 1), dev)
+    W = synth.device_normal((N5, K5), 0.02, synth.seed_of(5, 0, 2), "f32", dev)
+    qx, sx, qxt, sxt = E((T5, K5), u8), E((T5, nb(K5)), f32), E((K5, T5), u8), E((K5, nb(T5)), f32)
+    qdy, sdy, qdyt, sdyt = E((T5, N5), u8), E((T5, nb(N5)), f32), E((N5, T5), u8), E((N5, nb(T5)), f32)
+    qw, sw = E((N5, K5), u8), E((nb(N5), nb(K5)), f32)
+    Y, dX, dW = E((T5, N5), bf16), E((T5, K5), bf16), E((N5, K5), f32)
+    keep = [X, dY, W, qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, Y, dX, dW]
+    c5 = [qdual(X, T5, K5, qx, sx, qxt, sxt), qweight(W, N5, K5, qw, sw),
+          gemm(NT, T5, N5, K5, qx, K5, sx, qw, K5, sw, S128, Y, BF16, N5, keep),
+          qdual(dY, T5, N5, qdy, sdy, qdyt, sdyt),
+          gemm(NN, T5, K5, N5, qdy, N5, sdy, qw, K5, sw, S128, dX, BF16, K5, keep),
+          gemm(NT, N5, K5, T5, qdyt, T5, sdyt, qxt, T5, sxt, S1, dW, F32, K5, keep)]
+    runs.append(("5_outlier_stress", c5, 3 * 2.0 * T5 * N5 * K5, keep))
+    return runs
+
+
+def measure_configs(pf, torch, dev, sp, reps=20, warmup=5):
+    """Median time of each configuration's calls over `reps` repetitions, hot (back to back) and
+    cold (a 512 MiB buffer written before each repetition, outside the timed interval, to evict
+    the last-level cache).  Event-timed on the launch stream."""
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = {}
+    for name, calls, flops, keep in config_runs(pf, torch, dev, sp):
+        def once():
+            for fn, a in calls:
+                st = fn(*a)
+                if st:
+                    raise RuntimeError("%s: status %d" % (name, st))
+        for _ in range(warmup):
+            once()
+        res = {}
+        for mode in ("hot", "cold"):
+            ts = []
+            for _ in range(reps):
+                if mode == "cold":
+                    flush.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                once()
+                b.record(stream)
+                b.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            ts.sort()
+            med = ts[len(ts) // 2]
+            res[mode + "_us"] = round(med, 2)
+            res[mode + "_tflops"] = round(flops / (med * 1e-6) / 1e12, 1)
+        res["gflop"] = round(flops / 1e9, 3)
+        log("  config %-18s %10.3f GFLOP  hot %9.1f us (%6.1f TFLOP/s)  cold %9.1f us (%6.1f TFLOP/s)"
+            % (name, flops / 1e9, res["hot_us"], res["hot_tflops"], res["cold_us"], res["cold_tflops"]))
+        out[name] = res
+        del keep
+    return out
+
+
 def cpu_baseline(rows):
     """Time the oracle on a bounded sample of one layer of the same workload."""
     import numpy as np
@@ -303,6 +442,8 @@ def main():
     ap.add_argument("--layers", type=int, default=28, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-rows", type=int, default=16, help="rows per GEMM in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration timings (configs 1, 2, 3, 5 of the workload table)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one layer and a calibration copy for the memory counters, then exit")
     args = ap.parse_args()
@@ -377,6 +518,9 @@ def main():
             ("%.0f TFLOP/s" % (v[1] / v[0] / 1e9)) if v[1] else ("%.0f GB/s" % (v[2] / v[0] / 1e6))))
 
     side = {"swiglu_quant_dual": swiglu_side(pf, torch, dev, tokens, sp, args.steps)}
+    del plan, keep
+    torch.cuda.empty_cache()
+    configs = measure_configs(pf, torch, dev, sp) if not args.no_configs else None
 
     dom_name, dom = max(per_name.items(), key=lambda kv: kv[1][0])
     gemm_ms = per_kind["gemm"][0] / args.steps
@@ -415,6 +559,7 @@ def main():
         "breakdown_ms": {k: round(v[0] / args.steps, 3) for k, v in per_kind.items()},
         "roofline": roofline,
         "side_kernels": side,
+        "configs": configs,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample ...")

@@ -181,3 +181,47 @@ def device_normal(shape, std, seed, dtype, device):
     if std != 1.0:
         x.mul_(std)
     return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def _device_zero_blocks(x, gen, frac):
+    """Device form of zero_blocks (seeded by `gen`): zero a fraction of the 1x128 row segments and
+    of the 128-row column segments of x, in place."""
+    import torch
+    rows, cols = x.shape
+    rb, cb = rows // 128, cols // 128
+    lane = torch.arange(128, device=x.device)
+    k = int(round(frac * rows * cb))
+    if k:
+        sel = torch.randperm(rows * cb, generator=gen, device=x.device)[:k]
+        r, b = sel // cb, sel % cb
+        x[r[:, None].expand(-1, 128).reshape(-1), (b[:, None] * 128 + lane).reshape(-1)] = 0
+    k = int(round(frac * rb * cols))
+    if k:
+        sel = torch.randperm(rb * cols, generator=gen, device=x.device)[:k]
+        b, c = sel // cols, sel % cols
+        x[(b[:, None] * 128 + lane).reshape(-1), c[:, None].expand(-1, 128).reshape(-1)] = 0
+    return x
+
+
+def device_outlier_activations(tokens, channels, seed, device, frac_channels=0.01, factor=100.0,
+                               zero_frac=0.01):
+    """Device form of outlier_activations (torch's Philox stream; values differ from the host's)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((tokens, channels), generator=g, device=device, dtype=torch.float32)
+    pick = torch.randperm(channels, generator=g, device=device)[:int(round(frac_channels * channels))]
+    x[:, pick] *= factor
+    _device_zero_blocks(x, g, zero_frac)
+    return x.to(torch.bfloat16)
+
+
+def device_lognormal_gradients(tokens, channels, seed, device, mu=math.log(1e-6), sigma=2.0, zero_frac=0.01):
+    """Device form of lognormal_gradients (positive; torch's Philox stream)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((tokens, channels), generator=g, device=device, dtype=torch.float32)
+    x.mul_(sigma).add_(mu).exp_()
+    _device_zero_blocks(x, g, zero_frac)
+    return x.to(torch.bfloat16)
