@@ -4,13 +4,15 @@ One step = one micro-batch (2 x 4,096 = 8,192 tokens) through the linear
 layers of all 28 Transformer layers: the seven unfused projections
 (q, k, v, o, gate, up, down) in forward (Y = X W^T), data gradient
 (dX = dY W) and weight gradient (dW = dY^T X), with every quantiser inside
-the timed region: weights in 128x128 tiles, and each layer input X and each
-output gradient dY quantised both ways in one read (1x128 along features for
-the forward / data-gradient GEMM, 128-token blocks for the weight gradient).
-Products that a training step can run together share grouped launches
-(q/k/v, gate/up, and a layer's seven weight gradients); the data gradients of
-the q/k/v and of the gate/up projections are summed into their input's
-gradient in one pass.  Shapes come from the
+the timed region: weights in 128x128 tiles (a layer's seven in one launch),
+and each layer input X and each output gradient dY quantised both ways in one
+read (1x128 along features for the forward / data-gradient GEMM, 128-token
+blocks for the weight gradient).  The projections that read one input (q/k/v,
+gate/up) keep their weight codes in adjacent rows and their outputs and output
+gradients in adjacent columns, as fused QKV and gate/up projections do, so
+their forward products are one GEMM and the data gradient of their input (the
+sum of their products) is one GEMM over the concatenated K; a layer's seven
+weight gradients share one grouped launch.  Shapes come from the
 Puro-2B-Base model card (Qwen3-1.7B configuration: hidden 2,048, FFN 6,144,
 16 / 8 heads, 28 layers; sequence length 4,096, micro-batch 2).
 
@@ -59,7 +61,14 @@ class Plan:
 
 
 def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
-    """Allocate the stack's inputs (seeded, on the GPU) and outputs; return (plan, keepalive)."""
+    """Allocate the stack's inputs (seeded, on the GPU) and outputs; return (plan, keepalive).
+
+    The projections that read one input (q/k/v; gate/up) keep their weights' codes in adjacent
+    rows of one buffer and their outputs and output gradients in adjacent columns, as a fused
+    QKV or gate/up projection stores them.  Their forward products are then one GEMM, their
+    output gradients one dual-quantiser call, and the data gradient of their input, the sum of
+    their products, one GEMM over the concatenated K.  The products, codes and scales are those
+    of the separate projections: every 128-block boundary falls on a projection boundary."""
     import synth
     L = pf.lib()
     vp = ctypes.c_void_p
@@ -67,99 +76,110 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     plan = Plan()
     bf16, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
 
-    def P(t):
-        return vp(t.data_ptr())
+    def P(t, off=0):
+        return vp(t.data_ptr() + off)
 
     def nb(n):
         return (n + 127) // 128
 
+    T = tokens
+    shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
+    inputs = dict(synth.LAYER_INPUTS)
+    # per group: output width, input width, and each member's first row
+    grp = {}
+    for name, members, src in synth.PROJ_GROUPS:
+        rows, r0 = {}, 0
+        for g in members:
+            rows[g] = r0
+            r0 += shape[g][0]
+        grp[name] = (r0, inputs[src], src, members, rows)
+
     # Per-layer work buffers, reused by every layer.
-    qx = {name: torch.empty((tokens, c), dtype=u8, device=dev) for name, c in synth.LAYER_INPUTS}
-    sx = {name: torch.empty((tokens, nb(c)), dtype=f32, device=dev) for name, c in synth.LAYER_INPUTS}
-    qxt = {name: torch.empty((c, tokens), dtype=u8, device=dev) for name, c in synth.LAYER_INPUTS}
-    sxt = {name: torch.empty((c, nb(tokens)), dtype=f32, device=dev) for name, c in synth.LAYER_INPUTS}
-    qdy = {g: torch.empty((tokens, n), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    sdy = {g: torch.empty((tokens, nb(n)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    qdyt = {g: torch.empty((n, tokens), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    sdyt = {g: torch.empty((n, nb(tokens)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    qw = {g: torch.empty((n, k), dtype=u8, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    sw = {g: torch.empty((nb(n), nb(k)), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    y = {g: torch.empty((tokens, n), dtype=bf16, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    dx = {name: torch.empty((tokens, c), dtype=bf16, device=dev) for name, c in synth.LAYER_INPUTS}
+    qx = {x: torch.empty((T, c), dtype=u8, device=dev) for x, c in synth.LAYER_INPUTS}
+    sx = {x: torch.empty((T, nb(c)), dtype=f32, device=dev) for x, c in synth.LAYER_INPUTS}
+    qxt = {x: torch.empty((c, T), dtype=u8, device=dev) for x, c in synth.LAYER_INPUTS}
+    sxt = {x: torch.empty((c, nb(T)), dtype=f32, device=dev) for x, c in synth.LAYER_INPUTS}
+    qdy = {G: torch.empty((T, n), dtype=u8, device=dev) for G, (n, _, _, _, _) in grp.items()}
+    sdy = {G: torch.empty((T, nb(n)), dtype=f32, device=dev) for G, (n, _, _, _, _) in grp.items()}
+    qdyt = {G: torch.empty((n, T), dtype=u8, device=dev) for G, (n, _, _, _, _) in grp.items()}
+    sdyt = {G: torch.empty((n, nb(T)), dtype=f32, device=dev) for G, (n, _, _, _, _) in grp.items()}
+    qw = {G: torch.empty((n, k), dtype=u8, device=dev) for G, (n, k, _, _, _) in grp.items()}
+    sw = {G: torch.empty((nb(n), nb(k)), dtype=f32, device=dev) for G, (n, k, _, _, _) in grp.items()}
+    y = {G: torch.empty((T, n), dtype=bf16, device=dev) for G, (n, _, _, _, _) in grp.items()}
+    dx = {x: torch.empty((T, c), dtype=bf16, device=dev) for x, c in synth.LAYER_INPUTS}
     dw = {g: torch.empty((n, k), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, y, dx, dw]
 
     BF16, F32 = pf.PURO_BF16, pf.PURO_F32
     NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
     S1, S128 = pf.BGRAN["1x128"], pf.BGRAN["128x128"]
-    T = tokens
-    shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
 
     def grouped(layout, bgran, cdt, descs, name, flops):
         arr = (pf.GemmDesc * len(descs))(*descs)
         keep.append(arr)
         plan.add(L.puro_fp8_gemm_grouped, (layout, bgran, cdt, arr, len(descs), stream_ptr), "gemm", name, flops)
 
-    def fwd(g):
+    def dual(x, c, q, s, qt, st):
+        plan.add(L.puro_fp8_quant_dual, (P(x), BF16, T, c, c, P(q), c, P(s), 1, P(qt), T, P(st), stream_ptr),
+                 "quant_dual", "quant_dual", 0, T * c * (2 + 2 + 8 / 128))
+
+    def fwd(G):
+        n, k, src, _, _ = grp[G]
+        return pf.gemm_desc(T, n, [(k, P(qx[src]), k, P(sx[src]), P(qw[G]), k, P(sw[G]))], P(y[G]), n)
+
+    def dgrad(G):
+        # dX of the group's input = sum over its projections of dY_g W_g: one K loop over
+        # the adjacent output-gradient columns and weight rows
+        n, k, src, _, _ = grp[G]
+        return pf.gemm_desc(T, k, [(n, P(qdy[G]), n, P(sdy[G]), P(qw[G]), k, P(sw[G]))], P(dx[src]), k)
+
+    def wgrad(g, G):
         n, k, src = shape[g]
-        return pf.gemm_desc(T, n, [(k, P(qx[src]), k, P(sx[src]), P(qw[g]), k, P(sw[g]))], P(y[g]), n)
+        r0 = grp[G][4][g]
+        return pf.gemm_desc(n, k, [(T, P(qdyt[G], r0 * T), T, P(sdyt[G], r0 * nb(T) * 4),
+                                    P(qxt[src]), T, P(sxt[src]))], P(dw[g]), k)
 
-    def dgrad_sum(gs):
-        # dX of one input = sum over the projections reading it of dY_g W_g
-        k, src = shape[gs[0]][1], shape[gs[0]][2]
-        segs = [(shape[g][0], P(qdy[g]), shape[g][0], P(sdy[g]), P(qw[g]), k, P(sw[g])) for g in gs]
-        return pf.gemm_desc(T, k, segs, P(dx[src]), k)
+    def fl(G):
+        n, k = grp[G][0], grp[G][1]
+        return 2.0 * T * n * k
 
-    def wgrad(g):
-        n, k, src = shape[g]
-        return pf.gemm_desc(n, k, [(T, P(qdyt[g]), T, P(sdyt[g]), P(qxt[src]), T, P(sxt[src]))], P(dw[g]), k)
-
-    def fl(gs):
-        return sum(2.0 * T * shape[g][0] * shape[g][1] for g in gs)
-
-    # Products that can run together share one grouped launch, in the order a
-    # training step allows: the q, k and v projections of one input, the gate
-    # and up projections of one input; backward from the last projection to
-    # the first, the data gradients of projections that read the same input
-    # summed into that input's gradient in one pass (K segments); the weight
-    # gradients of a layer once its output gradients exist.
-    FWD_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
-    DGRAD_GROUPS = (("down",), ("gate", "up"), ("o",), ("q", "k", "v"))
+    group_of = {g: G for G, (_, _, _, members, _) in grp.items() for g in members}
     for layer in range(layers):
-        xs = {name: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
-              for i, (name, c) in enumerate(synth.LAYER_INPUTS)}
+        xs = {x: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
+              for i, (x, c) in enumerate(synth.LAYER_INPUTS)}
         wts = {g: synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
                for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
-        dys = {g: synth.device_normal((T, n), 1e-3, synth.seed_of(4, layer, 20 + j), "bf16", dev)
-               for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
+        dys = {G: synth.device_normal((T, grp[G][0]), 1e-3, synth.seed_of(4, layer, 30 + j), "bf16", dev)
+               for j, (G, _, _) in enumerate(synth.PROJ_GROUPS)}
         keep += [xs, wts, dys]
-        # forward: each weight quantised once (128x128 tiles), each distinct input
-        # once both ways (the 128-token copy is kept for the weight gradient)
-        # (the layer's seven weights in one grouped launch)
-        wd = (pf.QuantWeightDesc * len(synth.LAYER_GEMMS))(
-            *[pf.QuantWeightDesc(P(wts[g]), n, k, k, P(qw[g]), k, P(sw[g])) for g, n, k, _ in synth.LAYER_GEMMS])
+        # the layer's seven weights quantised in one grouped launch (128x128 tiles), each
+        # into its rows of its group's buffer
+        descs = []
+        for g, n, k, _ in synth.LAYER_GEMMS:
+            G = group_of[g]
+            r0 = grp[G][4][g]
+            descs.append(pf.QuantWeightDesc(P(wts[g]), n, k, k, P(qw[G], r0 * k), k,
+                                            P(sw[G], (r0 // 128) * nb(k) * 4)))
+        wd = (pf.QuantWeightDesc * len(descs))(*descs)
         keep.append(wd)
-        plan.add(L.puro_fp8_quant_weight_grouped, (F32, wd, len(synth.LAYER_GEMMS), stream_ptr),
+        plan.add(L.puro_fp8_quant_weight_grouped, (F32, wd, len(descs), stream_ptr),
                  "quant_weight", "quant_weight", 0,
                  sum(n * k * (4 + 1) + nb(n) * nb(k) * 4 for _, n, k, _ in synth.LAYER_GEMMS))
-        for name, c in synth.LAYER_INPUTS:
-            plan.add(L.puro_fp8_quant_dual, (P(xs[name]), BF16, T, c, c, P(qx[name]), c, P(sx[name]), 1,
-                                             P(qxt[name]), T, P(sxt[name]), stream_ptr),
-                     "quant_dual", "quant_dual", 0, T * c * (2 + 2 + 8 / 128))
-        for gs in FWD_GROUPS:
-            grouped(NT, S128, BF16, [fwd(g) for g in gs], "gemm_fwd_NT_128x128_bf16", fl(gs))
-        # backward: each output gradient quantised both ways in one read; data
-        # gradients dX = dY W with the forward's quantised W; weight gradients
-        # dW = dY^T X on the 128-token copies
-        for g in ("down", "gate", "up", "o", "q", "k", "v"):
-            n = shape[g][0]
-            plan.add(L.puro_fp8_quant_dual, (P(dys[g]), BF16, T, n, n, P(qdy[g]), n, P(sdy[g]), 1, P(qdyt[g]), T,
-                                             P(sdyt[g]), stream_ptr),
-                     "quant_dual", "quant_dual", 0, T * n * (2 + 2 + 8 / 128))
-        for gs in DGRAD_GROUPS:
-            grouped(NN, S128, BF16, [dgrad_sum(gs)], "gemm_dgrad_NN_128x128_bf16", fl(gs))
-        gs = [g for g, _, _, _ in synth.LAYER_GEMMS]
-        grouped(NT, S1, F32, [wgrad(g) for g in gs], "gemm_wgrad_NT_1x128_f32", fl(gs))
+        # forward: each input quantised once both ways (the 128-token copy is kept for the
+        # weight gradient), then its group's product
+        for G, _, src in synth.PROJ_GROUPS:
+            c = inputs[src]
+            dual(xs[src], c, qx[src], sx[src], qxt[src], sxt[src])
+            grouped(NT, S128, BF16, [fwd(G)], "gemm_fwd_NT_128x128_bf16", fl(G))
+        # backward, from the last group to the first: the group's output gradient quantised
+        # both ways in one read, then the data gradient of its input with the forward's
+        # quantised weights; the seven weight gradients once all output gradients exist
+        for G, _, _ in reversed(synth.PROJ_GROUPS):
+            n = grp[G][0]
+            dual(dys[G], n, qdy[G], sdy[G], qdyt[G], sdyt[G])
+            grouped(NN, S128, BF16, [dgrad(G)], "gemm_dgrad_NN_128x128_bf16", fl(G))
+        grouped(NT, S1, F32, [wgrad(g, group_of[g]) for g, _, _, _ in synth.LAYER_GEMMS],
+                "gemm_wgrad_NT_1x128_f32", sum(2.0 * T * n * k for _, n, k, _ in synth.LAYER_GEMMS))
     return plan, keep
 
 

@@ -59,6 +59,11 @@ LAYER_INPUTS = [("x_attn", HIDDEN), ("x_o", Q_HEADS * HEAD_DIM), ("x_mlp", HIDDE
 # The fused four-GEMM view of the same layer (QKV, O, gate_up, down): (N_out, K_in)
 FUSED_GEMMS = [("qkv", 4096, 2048), ("o", 2048, 2048), ("gate_up", 12288, 2048), ("down", 2048, 6144)]
 
+# Projections that read the same input, in the order in which their weights' rows (and their
+# outputs' and output gradients' columns) are stored side by side: (group, members, input)
+PROJ_GROUPS = [("qkv", ("q", "k", "v"), "x_attn"), ("o", ("o",), "x_o"),
+               ("gate_up", ("gate", "up"), "x_mlp"), ("down", ("down",), "h")]
+
 
 def seed_of(config, layer=0, tensor_id=0):
     return 1_000_003 * config + 1_009 * layer + tensor_id

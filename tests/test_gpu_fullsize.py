@@ -216,3 +216,78 @@ def test_layer_grouped_full_size(dev):
     for g, dW in zip(gs, dWs):
         seed += 1
         _check_sampled("NT", "1x128", host_q["dY_" + g][2:] + host_q[shape[g][2]][2:], dW, T, seed, torch.float32)
+
+
+def test_layer_adjacent_full_size(dev):
+    """One whole layer at 8,192 tokens as the benchmark's step runs it: the q/k/v and gate/up
+    weights quantised into adjacent rows of one buffer per group (the seven weights in one
+    launch), each group's output gradient quantised both ways in one call, each group's forward
+    product one GEMM, the data gradient of each input one GEMM over the group's concatenated K,
+    and the seven weight gradients, on row ranges of the groups' token-blocked copies, in one
+    launch.  Codes and scales byte-compared over whole tensors; products on sampled entries."""
+    T = synth.TOKENS
+    shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
+    inputs = dict(synth.LAYER_INPUTS)
+    host_q, dev_q = {}, {}
+
+    def dual(name, x):
+        d = pf.puro_fp8_quant_dual(to_dev(x), True)
+        r = oracle.quant_act(x) + oracle.quant_transpose(x, True)
+        torch.cuda.synchronize()
+        for t, ref, what in zip(d, r, ("q_row", "s_row", "q_tok", "s_tok")):
+            _same(t, ref, (name, what))
+        host_q[name], dev_q[name] = r, d
+
+    for i, (name, c) in enumerate(synth.LAYER_INPUTS):
+        dual(name, synth.normal((T, c), 1.0, synth.seed_of(4, 0, i), "bf16"))
+    rows, width = {}, {}
+    for G, members, _ in synth.PROJ_GROUPS:
+        r0 = 0
+        for g in members:
+            rows[g] = (G, r0)
+            r0 += shape[g][0]
+        width[G] = r0
+    for j, (G, _, _) in enumerate(synth.PROJ_GROUPS):
+        dual("dY_" + G, synth.normal((T, width[G]), 1e-3, synth.seed_of(4, 0, 30 + j), "bf16"))
+    # the seven weights in one launch, each into its rows of its group's buffers
+    qwG = {G: torch.empty((width[G], inputs[src]), dtype=torch.uint8, device=dev) for G, _, src in synth.PROJ_GROUPS}
+    swG = {G: torch.empty((width[G] // 128, inputs[src] // 128), dtype=torch.float32, device=dev)
+           for G, _, src in synth.PROJ_GROUPS}
+    Ws, outs, gs = {}, [], [g for g, _, _, _ in synth.LAYER_GEMMS]
+    for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS):
+        Ws[g] = synth.normal((n, k), 0.02, synth.seed_of(4, 0, 10 + j))
+        G, r0 = rows[g]
+        outs.append((qwG[G][r0:r0 + n], swG[G][r0 // 128:(r0 + n) // 128]))
+    pf.puro_fp8_quant_weight_grouped([to_dev(Ws[g]) for g in gs], outs=outs)
+    torch.cuda.synchronize()
+    hq, hs = {}, {}
+    for G, members, _ in synth.PROJ_GROUPS:
+        refs = [oracle.quant_weight(Ws[g]) for g in members]
+        hq[G] = np.concatenate([r[0] for r in refs])
+        hs[G] = np.concatenate([r[1] for r in refs])
+        _same(qwG[G], hq[G], ("qW", G))
+        _same(swG[G], hs[G], ("sW", G))
+
+    seed = 100
+    for G, _, src in synth.PROJ_GROUPS:
+        (hqx, hsx), (dqx, dsx) = host_q[src][:2], dev_q[src][:2]
+        (Y,) = pf.puro_fp8_gemm_grouped("NT", [(dqx, dsx, qwG[G], swG[G])], out_dtype=torch.bfloat16)
+        (dX,) = pf.puro_fp8_gemm_grouped("NN", [dev_q["dY_" + G][:2] + (qwG[G], swG[G])], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        _check_sampled("NT", "128x128", (hqx, hsx, hq[G], hs[G]), Y, inputs[src], seed + 1, torch.bfloat16)
+        _check_sampled("NN", "128x128", host_q["dY_" + G][:2] + (hq[G], hs[G]), dX, width[G], seed + 2,
+                       torch.bfloat16)
+        seed += 2
+    probs, hprobs = [], []
+    for g in gs:
+        n, k, src = shape[g]
+        G, r0 = rows[g]
+        qt, st = dev_q["dY_" + G][2:]
+        hqt, hst = host_q["dY_" + G][2:]
+        probs.append((qt[r0:r0 + n], st[r0:r0 + n]) + dev_q[src][2:])
+        hprobs.append((hqt[r0:r0 + n], hst[r0:r0 + n]) + host_q[src][2:])
+    dWs = pf.puro_fp8_gemm_grouped("NT", probs, bgran="1x128", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for g, dW, hp in zip(gs, dWs, hprobs):
+        seed += 1
+        _check_sampled("NT", "1x128", hp, dW, T, seed, torch.float32)
