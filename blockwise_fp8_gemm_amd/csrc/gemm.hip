@@ -553,45 +553,19 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     const float *sc0_base;
     int64_t sc0_step;
     scale_source(seg0, sc0_base, sc0_step);
-    // Several segments: block v belongs to the segment whose first block is
-    // the largest one <= v (a switch, so that every read of the argument block
-    // has a constant index and stays in scalar registers).
-    static_assert(kMaxKSeg == 4, "segment lookup below");
-    int64_t seg_start[4];   // first block of each segment; past-the-end ones never match
-    seg_start[0] = 0;
-    seg_start[1] = MULTI && p.nseg > 1 ? p.seg[0].KB : INT64_MAX;
-    seg_start[2] = MULTI && p.nseg > 2 ? seg_start[1] + p.seg[1].KB : INT64_MAX;
-    seg_start[3] = MULTI && p.nseg > 3 ? seg_start[2] + p.seg[2].KB : INT64_MAX;
     auto stage = [&](int64_t v, uint8_t *L, float *LSC) {
-        if (!MULTI) {
-            stage_seg(seg0, v, sc0_base + v * sc0_step, L, LSC);
-            return;
-        }
-        const int si = (v >= seg_start[1]) + (v >= seg_start[2]) + (v >= seg_start[3]);
-        KSeg sg;
-        int64_t kb;
-        switch (si) {
-        case 0: sg = p.seg[0]; kb = v; break;
-        case 1: sg = p.seg[1]; kb = v - seg_start[1]; break;
-        case 2: sg = p.seg[2]; kb = v - seg_start[2]; break;
-        default: sg = p.seg[3]; kb = v - seg_start[3]; break;
-        }
-        const float *base;
-        int64_t step;
-        scale_source(sg, base, step);
-        stage_seg(sg, kb, base + kb * step, L, LSC);
+        stage_seg(seg0, v, sc0_base + v * sc0_step, L, LSC);
     };
 
-    const int64_t lo = kb_lo, hi = kb_hi;
-    if (lo < hi)
-        stage(lo, lds0, lds_sc0);
-    // K block kb computed from stage (L, LSC) while block kb + 1 is copied
-    // into the other stage (LN, LSCN).
-    auto kblock = [&](int64_t kb, const uint8_t *L, const float *LSC, uint8_t *LN, float *LSCN) {
+    // K block kb of a run of blocks [.., end) with fixed operands, computed
+    // from stage (L, LSC) while the run's block kb + 1 is copied into the
+    // other stage (LN, LSCN) by stg.
+    auto kblock = [&](auto &&stg, int64_t kb, int64_t end, const uint8_t *L, const float *LSC, uint8_t *LN,
+                      float *LSCN) {
         __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of block kb have landed
         __syncthreads();   // everyone's have; block kb-1 (in LN) is no longer read
-        if (kb + 1 < hi)
-            stage(kb + 1, LN, LSCN);
+        if (kb + 1 < end)
+            stg(kb + 1, LN, LSCN);
 
         const uint8_t *ta = L;
         const uint8_t *tb = L + A_BYTES;
@@ -696,17 +670,50 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             }
         }
     };
-    if constexpr (Cfg::STATIC_STAGES) {
-        for (int64_t kb = lo; kb < hi; kb += 2) {
-            kblock(kb, lds0, lds_sc0, lds1, lds_sc1);
-            if (kb + 1 < hi)
-                kblock(kb + 1, lds1, lds_sc1, lds0, lds_sc0);
+    // Blocks [b0, b1) of one run: the first is staged into stage 0, then each
+    // is computed while the next is copied.
+    auto run = [&](auto &&stg, int64_t b0, int64_t b1) {
+        if (b0 < b1)
+            stg(b0, lds0, lds_sc0);
+        if constexpr (Cfg::STATIC_STAGES) {
+            for (int64_t kb = b0; kb < b1; kb += 2) {
+                kblock(stg, kb, b1, lds0, lds_sc0, lds1, lds_sc1);
+                if (kb + 1 < b1)
+                    kblock(stg, kb + 1, b1, lds1, lds_sc1, lds0, lds_sc0);
+            }
+        } else {
+            // stage chosen at run time: every read of a stage waits for the copies in flight
+            for (int64_t kb = b0; kb < b1; kb++) {
+                const bool odd = ((kb - b0) & 1) != 0;
+                kblock(stg, kb, b1, odd ? lds1 : lds0, odd ? lds_sc1 : lds_sc0, odd ? lds0 : lds1,
+                       odd ? lds_sc0 : lds_sc1);
+            }
         }
+    };
+    if constexpr (!MULTI) {
+        run(stage, kb_lo, kb_hi);
     } else {
-        // stage chosen at run time: every read of a stage waits for the copies in flight
-        for (int64_t kb = lo; kb < hi; kb++) {
-            const bool odd = ((kb - lo) & 1) != 0;
-            kblock(kb, odd ? lds1 : lds0, odd ? lds_sc1 : lds_sc0, odd ? lds0 : lds1, odd ? lds_sc0 : lds_sc1);
+        // Several segments (the whole K range): one run per segment, so that the
+        // K loop of each has its operands and scale source fixed.  A segment's
+        // fields are picked with a constant index (they stay in scalar
+        // registers); between runs every wave finishes the previous run's last
+        // block before its stage is refilled.
+        static_assert(kMaxKSeg == 4, "segment selection below");
+        for (int si = 0; si < p.nseg; si++) {
+            KSeg sg;
+            switch (si) {
+            case 0: sg = p.seg[0]; break;
+            case 1: sg = p.seg[1]; break;
+            case 2: sg = p.seg[2]; break;
+            default: sg = p.seg[3]; break;
+            }
+            const float *scb;
+            int64_t step;
+            scale_source(sg, scb, step);
+            auto stg = [&](int64_t kb, uint8_t *L, float *LSC) { stage_seg(sg, kb, scb + kb * step, L, LSC); };
+            if (si > 0)
+                __syncthreads();
+            run(stg, 0, sg.KB);
         }
     }
 
