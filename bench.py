@@ -105,10 +105,12 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     sdyt = {G: torch.empty((n, nb(T)), dtype=f32, device=dev) for G, (n, _, _, _, _) in grp.items()}
     qw = {G: torch.empty((n, k), dtype=u8, device=dev) for G, (n, k, _, _, _) in grp.items()}
     sw = {G: torch.empty((nb(n), nb(k)), dtype=f32, device=dev) for G, (n, k, _, _, _) in grp.items()}
+    qwt = {G: torch.empty((k, n), dtype=u8, device=dev) for G, (n, k, _, _, _) in grp.items()}
+    swt = {G: torch.empty((nb(k), nb(n)), dtype=f32, device=dev) for G, (n, k, _, _, _) in grp.items()}
     y = {G: torch.empty((T, n), dtype=bf16, device=dev) for G, (n, _, _, _, _) in grp.items()}
     dx = {x: torch.empty((T, c), dtype=bf16, device=dev) for x, c in synth.LAYER_INPUTS}
     dw = {g: torch.empty((n, k), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
-    keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, y, dx, dw]
+    keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, qwt, swt, y, dx, dw]
 
     BF16, F32 = pf.PURO_BF16, pf.PURO_F32
     NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
@@ -129,9 +131,10 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
 
     def dgrad(G):
         # dX of the group's input = sum over its projections of dY_g W_g: one K loop over
-        # the adjacent output-gradient columns and weight rows
+        # the adjacent output-gradient columns and weight rows, with the weights' codes
+        # read from their transposed copy (NT: K-contiguous like the forward's operands)
         n, k, src, _, _ = grp[G]
-        return pf.gemm_desc(T, k, [(n, P(qdy[G]), n, P(sdy[G]), P(qw[G]), k, P(sw[G]))], P(dx[src]), k)
+        return pf.gemm_desc(T, k, [(n, P(qdy[G]), n, P(sdy[G]), P(qwt[G]), n, P(swt[G]))], P(dx[src]), k)
 
     def wgrad(g, G):
         n, k, src = shape[g]
@@ -147,24 +150,24 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     for layer in range(layers):
         xs = {x: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
               for i, (x, c) in enumerate(synth.LAYER_INPUTS)}
-        wts = {g: synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
-               for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS)}
+        # FP32 master weights, those of one group in adjacent rows of one tensor
+        wts = {G: torch.empty((n, k), dtype=f32, device=dev) for G, (n, k, _, _, _) in grp.items()}
+        for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS):
+            G = group_of[g]
+            r0 = grp[G][4][g]
+            wts[G][r0:r0 + n] = synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
         dys = {G: synth.device_normal((T, grp[G][0]), 1e-3, synth.seed_of(4, layer, 30 + j), "bf16", dev)
                for j, (G, _, _) in enumerate(synth.PROJ_GROUPS)}
         keep += [xs, wts, dys]
-        # the layer's seven weights quantised in one grouped launch (128x128 tiles), each
-        # into its rows of its group's buffer
-        descs = []
-        for g, n, k, _ in synth.LAYER_GEMMS:
-            G = group_of[g]
-            r0 = grp[G][4][g]
-            descs.append(pf.QuantWeightDesc(P(wts[g]), n, k, k, P(qw[G], r0 * k), k,
-                                            P(sw[G], (r0 // 128) * nb(k) * 4)))
+        # the layer's weights quantised in one grouped launch (128x128 tiles; the tiles of a
+        # group's weights are those of each weight), each group's codes also transposed
+        descs = [pf.QuantWeightDesc(P(wts[G]), n, k, k, P(qw[G]), k, P(sw[G]), P(qwt[G]), n, P(swt[G]))
+                 for G, (n, k, _, _, _) in grp.items()]
         wd = (pf.QuantWeightDesc * len(descs))(*descs)
         keep.append(wd)
         plan.add(L.puro_fp8_quant_weight_grouped, (F32, wd, len(descs), stream_ptr),
                  "quant_weight", "quant_weight", 0,
-                 sum(n * k * (4 + 1) + nb(n) * nb(k) * 4 for _, n, k, _ in synth.LAYER_GEMMS))
+                 sum(n * k * (4 + 2) + 2 * nb(n) * nb(k) * 4 for _, n, k, _ in synth.LAYER_GEMMS))
         # forward: each input quantised once both ways (the 128-token copy is kept for the
         # weight gradient), then its group's product
         for G, _, src in synth.PROJ_GROUPS:
@@ -177,7 +180,7 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
         for G, _, _ in reversed(synth.PROJ_GROUPS):
             n = grp[G][0]
             dual(dys[G], n, qdy[G], sdy[G], qdyt[G], sdyt[G])
-            grouped(NN, S128, BF16, [dgrad(G)], "gemm_dgrad_NN_128x128_bf16", fl(G))
+            grouped(NT, S128, BF16, [dgrad(G)], "gemm_dgrad_NT_128x128_bf16", fl(G))
         grouped(NT, S1, F32, [wgrad(g, group_of[g]) for g, _, _, _ in synth.LAYER_GEMMS],
                 "gemm_wgrad_NT_1x128_f32", sum(2.0 * T * n * k for _, n, k, _ in synth.LAYER_GEMMS))
     return plan, keep

@@ -58,7 +58,8 @@ class GemmDesc(ctypes.Structure):
 class QuantWeightDesc(ctypes.Structure):
     """puro_quant_weight_desc_t: one weight of puro_fp8_quant_weight_grouped."""
     _fields_ = [("w", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ldw", ctypes.c_int64),
-                ("q", ctypes.c_void_p), ("ldq", ctypes.c_int64), ("s", ctypes.c_void_p)]
+                ("q", ctypes.c_void_p), ("ldq", ctypes.c_int64), ("s", ctypes.c_void_p),
+                ("qt", ctypes.c_void_p), ("ldqt", ctypes.c_int64), ("st", ctypes.c_void_p)]
 
 
 def gemm_desc(M, N, segments, C, ldc, accumulate=False):
@@ -221,29 +222,44 @@ def puro_fp8_quant_weight(w, q=None, s=None, stream=None, pow2=False):
     return q, s
 
 
-def puro_fp8_quant_weight_grouped(weights, outs=None, stream=None, pow2=False):
+def puro_fp8_quant_weight_grouped(weights, outs=None, stream=None, pow2=False, transposed=False):
     """128x128 tiles of several weights (one dtype) in as few launches as possible.
 
-    weights: list of 2-D tensors; outs: optional list of (q, s) to write into.
-    Returns the list of (q, s), each as puro_fp8_quant_weight would return it.
+    weights: list of 2-D tensors; outs: optional list of (q, s), or (q, s, qt, st) with
+    transposed, to write into.  transposed: also write each weight's codes and scales
+    transposed (qt [cols][rows], st [ceil(cols/128)][ceil(rows/128)]).
+    Returns the list of (q, s), or of (q, s, qt, st) with transposed.
     """
     if outs is None:
-        outs = [(None, None)] * len(weights)
+        outs = [(None,) * (4 if transposed else 2)] * len(weights)
     if len(outs) != len(weights):
-        raise ValueError("outs must have one (q, s) per weight")
+        raise ValueError("outs must have one entry per weight")
     if any(w.dtype != weights[0].dtype for w in weights):
         raise ValueError("all weights must share one dtype")
     res, descs = [], []
-    for w, (q, s) in zip(weights, outs):
+    for w, o in zip(weights, outs):
         rows, cols = w.shape
+        q, s = o[0], o[1]
         if q is None:
             q = empty_2d(rows, cols, torch.uint8, w.device)
         if s is None:
             s = torch.empty((_nblk(rows), _nblk(cols)), dtype=torch.float32, device=w.device)
         _need(q, (rows, cols), torch.uint8, "q")
         _need_dense(s, (_nblk(rows), _nblk(cols)), "s")
-        descs.append(QuantWeightDesc(_ptr(w), rows, cols, _ld(w), _ptr(q), _ld(q), _ptr(s)))
-        res.append((q, s))
+        if transposed:
+            qt, st = (o[2], o[3]) if len(o) == 4 else (None, None)
+            if qt is None:
+                qt = empty_2d(cols, rows, torch.uint8, w.device)
+            if st is None:
+                st = torch.empty((_nblk(cols), _nblk(rows)), dtype=torch.float32, device=w.device)
+            _need(qt, (cols, rows), torch.uint8, "qt")
+            _need_dense(st, (_nblk(cols), _nblk(rows)), "st")
+            descs.append(QuantWeightDesc(_ptr(w), rows, cols, _ld(w), _ptr(q), _ld(q), _ptr(s),
+                                         _ptr(qt), _ld(qt), _ptr(st)))
+            res.append((q, s, qt, st))
+        else:
+            descs.append(QuantWeightDesc(_ptr(w), rows, cols, _ld(w), _ptr(q), _ld(q), _ptr(s), None, 0, None))
+            res.append((q, s))
     if not descs:
         return res
     arr = (QuantWeightDesc * len(descs))(*descs)

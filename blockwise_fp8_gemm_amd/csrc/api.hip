@@ -99,12 +99,18 @@ static puro_status_t quant_weight_grouped_impl(puro_dtype_t wdt, const puro_quan
         v.reserve((size_t)count);
         for (int i = 0; i < count; i++) {
             const puro_quant_weight_desc_t &d = items[i];
-            const puro_status_t st = check_quant(d.w, wdt, d.rows, d.cols, d.ldw, d.q, d.ldq, d.cols, d.s);
+            puro_status_t st = check_quant(d.w, wdt, d.rows, d.cols, d.ldw, d.q, d.ldq, d.cols, d.s);
             if (st != PURO_OK)
                 return st;
+            if (d.qt) {   // transposed copy: qt [cols][rows], st [ceil(cols/128)][ceil(rows/128)]
+                st = check_quant(d.w, wdt, d.rows, d.cols, d.ldw, d.qt, d.ldqt, d.rows, d.st);
+                if (st != PURO_OK)
+                    return st;
+            }
             if (d.rows == 0 || d.cols == 0)
                 continue;
-            v.push_back({d.w, d.rows, d.cols, d.ldw, d.q, d.ldq, d.s, (d.cols + 127) / 128});
+            v.push_back({d.w, d.rows, d.cols, d.ldw, d.q, d.ldq, d.s, (d.cols + 127) / 128, d.qt,
+                         d.qt ? d.ldqt : 0, d.qt ? d.st : nullptr, (d.rows + 127) / 128});
         }
         if (v.empty())
             return PURO_OK;

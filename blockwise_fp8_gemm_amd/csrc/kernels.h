@@ -22,7 +22,11 @@ struct QuantWeightItem {
     uint8_t *q;
     int64_t ldq;
     float *s;
-    int64_t cb;
+    int64_t cb;        // ceil(cols / 128)
+    uint8_t *qt;       // transposed codes [cols][rows] (row stride ldqt), or NULL
+    int64_t ldqt;
+    float *st;         // transposed scales [cb][rb], dense (with qt)
+    int64_t rb;        // ceil(rows / 128)
 };
 constexpr int kQuantGroupMax = 16;   // weights per launch; more take several launches
 hipError_t launch_quant_weight_group(const QuantWeightItem *items, int count, bool bf16, bool pow2,

@@ -93,13 +93,18 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const T *__restrict__ x,
 // cross-lane max per wave, then across the 16 waves through LDS.
 // ---------------------------------------------------------------------------
 // Tile (tx, ty) of one weight: columns [128 tx, +128) x rows [128 ty, +128).
+// With qt, the tile's codes are also written transposed, to qt[c][r] (row
+// stride ldqt), and its scale to st[tx][ty] (rb = tile rows of the weight).
 template <typename T>
 __device__ __forceinline__ void quant_weight_tile(const T *__restrict__ w, int64_t rows, int64_t cols,
                                                   int64_t ldw, uint8_t *__restrict__ q, int64_t ldq,
                                                   float *__restrict__ s, int64_t cb, int64_t tx,
-                                                  int64_t ty, int pow2)
+                                                  int64_t ty, int pow2, uint8_t *__restrict__ qt = nullptr,
+                                                  int64_t ldqt = 0, float *__restrict__ st = nullptr,
+                                                  int64_t rb = 0)
 {
     __shared__ float red[16];
+    __shared__ uint8_t tt[128][128 + 4];   // transposed codes [column][row], padded rows
     const int t = threadIdx.x;
     const int cc = t & 15, rg = t >> 4;
     const int64_t r0 = ty * 128, cbase = tx * 128;
@@ -152,9 +157,32 @@ __device__ __forceinline__ void quant_weight_tile(const T *__restrict__ w, int64
                 if (c0 + j < cols)
                     qr[c0 + j] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFF);
         }
+        if (qt) {
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                tt[cc * 8 + j][rg + 64 * i] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFF);
+        }
     }
-    if (t == 0)
+    if (t == 0) {
         s[ty * cb + tx] = sc;
+        if (qt)
+            st[tx * rb + ty] = sc;
+    }
+    if (qt) {
+        // thread t writes bytes [16 (t % 8), +16) of transposed row t / 8
+        __syncthreads();
+        const int c = t >> 3, sg = t & 7;
+        const int64_t cg = cbase + c, rs = r0 + 16 * sg;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(&tt[c][16 * sg]);
+        uint8_t *dst = qt + cg * ldqt + rs;
+        if (full_tile) {
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(src[0], src[1], src[2], src[3]);
+        } else if (cg < cols) {
+            for (int e = 0; e < 16; e++)
+                if (rs + e < rows)
+                    dst[e] = tt[c][16 * sg + e];
+        }
+    }
 }
 
 template <typename T>
@@ -188,7 +216,8 @@ __global__ __launch_bounds__(1024) void quant_weight_group_kernel(QuantWeightGro
     i = __builtin_amdgcn_readfirstlane(i);   // uniform: the item's fields stay in scalar registers
     const int64_t local = b - g->first[i], cb = g->it[i].cb;
     quant_weight_tile<T>((const T *)g->it[i].w, g->it[i].rows, g->it[i].cols, g->it[i].ldw, g->it[i].q,
-                         g->it[i].ldq, g->it[i].s, cb, local % cb, local / cb, g->pow2);
+                         g->it[i].ldq, g->it[i].s, cb, local % cb, local / cb, g->pow2, g->it[i].qt,
+                         g->it[i].ldqt, g->it[i].st, g->it[i].rb);
 }
 
 // ---------------------------------------------------------------------------

@@ -111,6 +111,11 @@ puro_status_t puro_fp8_quant_weight(const void *w, puro_dtype_t wdt, int64_t row
  * Every item is validated as a puro_fp8_quant_weight call before anything is
  * enqueued, and the first failing item's status is returned.  No output may
  * overlap another item's output or any input.
+ * With qt not NULL an item also gets its codes and scales transposed (qt, st;
+ * validated like q and s, with rows and cols swapped): the B operand of the
+ * data-gradient product dX = dY W in NT form, read by the matrix cores in the
+ * same K-contiguous order as the forward's.  qt = NULL: no transposed copy
+ * (ldqt and st are ignored).
  */
 #define PURO_QUANT_MAX_GROUP 4096
 typedef struct {
@@ -119,6 +124,9 @@ typedef struct {
     uint8_t *q;               /* [rows][cols] codes, row stride ldq */
     int64_t ldq;
     float *s;                 /* [ceil(rows/128)][ceil(cols/128)], dense */
+    uint8_t *qt;              /* NULL, or the same codes transposed: [cols][rows], row stride ldqt */
+    int64_t ldqt;
+    float *st;                /* with qt: the scales transposed, [ceil(cols/128)][ceil(rows/128)], dense */
 } puro_quant_weight_desc_t;
 puro_status_t puro_fp8_quant_weight_grouped(puro_dtype_t wdt, const puro_quant_weight_desc_t *items,
                                             int count, hipStream_t stream);

@@ -288,4 +288,10 @@ def test_quant_weight_grouped_validation(name):
     assert call([good, D(NUL, 256, 256, 256, P, 256, P)]) == NULL
     assert call([good, D(P, 256, 256, 256, P, 256, NUL)]) == NULL
     assert call([D(P, -1, 256, 256, P, 256, P), D(NUL, 4, 4, 16, P, 16, P)]) == SHAPE
+    # the transposed copy [cols][rows] is checked like the codes, rows and cols swapped
+    assert call([D(P, 256, 384, 384, P, 384, P, P, 128, P)]) == SHAPE     # ldqt < rows
+    assert call([D(P, 256, 384, 384, P, 384, P, P, 264, P)]) == ALIGN     # ldqt not a multiple of 16
+    assert call([D(P, 256, 384, 384, P, 384, P, P_ODD, 256, P)]) == ALIGN
+    assert call([D(P, 256, 384, 384, P, 384, P, P, 256, NUL)]) == NULL    # st missing
+    assert call([D(NUL, 0, 384, 384, NUL, 384, NUL, P, 0, NUL)]) == OK    # empty weight: nothing
 

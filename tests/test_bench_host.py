@@ -41,7 +41,7 @@ def test_traffic_lookup_follows_the_kernel_source(tmp_path, monkeypatch):
                  "kernel source sha256: %s (gemm.hip, then common.h)\n" % good)
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.measured_traffic("gemm_fwd_NT_128x128_bf16") == 3.0002e8
-    assert bench.measured_traffic("gemm_dgrad_NN_128x128_bf16") is None      # no row
+    assert bench.measured_traffic("gemm_dgrad_NT_128x128_bf16") is None      # no row
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)      # kernel changed
     assert bench.measured_traffic("gemm_fwd_NT_128x128_bf16") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
@@ -50,7 +50,7 @@ def test_traffic_lookup_follows_the_kernel_source(tmp_path, monkeypatch):
 
 def test_committed_traffic_matches_committed_kernels():
     """The committed profile was taken on the committed GEMM source (else the bench reports null)."""
-    for kind in ("gemm_fwd_NT_128x128_bf16", "gemm_dgrad_NN_128x128_bf16", "gemm_wgrad_NT_1x128_f32"):
+    for kind in ("gemm_fwd_NT_128x128_bf16", "gemm_dgrad_NT_128x128_bf16", "gemm_wgrad_NT_1x128_f32"):
         assert bench.measured_traffic(kind) is not None, kind
 
 

@@ -220,11 +220,13 @@ def test_layer_grouped_full_size(dev):
 
 def test_layer_adjacent_full_size(dev):
     """One whole layer at 8,192 tokens as the benchmark's step runs it: the q/k/v and gate/up
-    weights quantised into adjacent rows of one buffer per group (the seven weights in one
-    launch), each group's output gradient quantised both ways in one call, each group's forward
-    product one GEMM, the data gradient of each input one GEMM over the group's concatenated K,
-    and the seven weight gradients, on row ranges of the groups' token-blocked copies, in one
-    launch.  Codes and scales byte-compared over whole tensors; products on sampled entries."""
+    weights quantised into adjacent rows of one buffer per group (each weight as an item, and
+    each group's adjacent master weights as one item with its transposed copy: the same codes),
+    each group's output gradient quantised both ways in one call, each group's forward product
+    one GEMM, the data gradient of each input one NT GEMM over the group's concatenated K on the
+    transposed codes, and the seven weight gradients, on row ranges of the groups' token-blocked
+    copies, in one launch.  Codes and scales byte-compared over whole tensors; products on
+    sampled entries against the oracle's NT / NN definitions."""
     T = synth.TOKENS
     shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
     inputs = dict(synth.LAYER_INPUTS)
@@ -259,22 +261,34 @@ def test_layer_adjacent_full_size(dev):
         G, r0 = rows[g]
         outs.append((qwG[G][r0:r0 + n], swG[G][r0 // 128:(r0 + n) // 128]))
     pf.puro_fp8_quant_weight_grouped([to_dev(Ws[g]) for g in gs], outs=outs)
+    # the benchmark quantises each group's adjacent master weights as one weight, with the
+    # transposed copy its data gradient reads: the same tiles, so the same codes and scales
+    WG = {G: np.concatenate([Ws[g] for g in members]) for G, members, _ in synth.PROJ_GROUPS}
+    G4 = [G for G, _, _ in synth.PROJ_GROUPS]
+    tq = pf.puro_fp8_quant_weight_grouped([to_dev(WG[G]) for G in G4], transposed=True)
     torch.cuda.synchronize()
-    hq, hs = {}, {}
-    for G, members, _ in synth.PROJ_GROUPS:
+    hq, hs, qwtG, swtG = {}, {}, {}, {}
+    for (G, members, _), (q4, s4, qt4, st4) in zip(synth.PROJ_GROUPS, tq):
         refs = [oracle.quant_weight(Ws[g]) for g in members]
         hq[G] = np.concatenate([r[0] for r in refs])
         hs[G] = np.concatenate([r[1] for r in refs])
         _same(qwG[G], hq[G], ("qW", G))
         _same(swG[G], hs[G], ("sW", G))
+        _same(q4, hq[G], ("qW whole group", G))
+        _same(s4, hs[G], ("sW whole group", G))
+        _same(qt4, np.ascontiguousarray(hq[G].T), ("qW transposed", G))
+        _same(st4, np.ascontiguousarray(hs[G].T), ("sW transposed", G))
+        qwtG[G], swtG[G] = qt4, st4
 
     seed = 100
     for G, _, src in synth.PROJ_GROUPS:
         (hqx, hsx), (dqx, dsx) = host_q[src][:2], dev_q[src][:2]
         (Y,) = pf.puro_fp8_gemm_grouped("NT", [(dqx, dsx, qwG[G], swG[G])], out_dtype=torch.bfloat16)
-        (dX,) = pf.puro_fp8_gemm_grouped("NN", [dev_q["dY_" + G][:2] + (qwG[G], swG[G])], out_dtype=torch.bfloat16)
+        (dX,) = pf.puro_fp8_gemm_grouped("NT", [dev_q["dY_" + G][:2] + (qwtG[G], swtG[G])],
+                                         out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
         _check_sampled("NT", "128x128", (hqx, hsx, hq[G], hs[G]), Y, inputs[src], seed + 1, torch.bfloat16)
+        # dX = dY W: the oracle's NN product of the untransposed codes
         _check_sampled("NN", "128x128", host_q["dY_" + G][:2] + (hq[G], hs[G]), dX, width[G], seed + 2,
                        torch.bfloat16)
         seed += 2

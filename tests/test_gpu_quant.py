@@ -107,10 +107,13 @@ def test_quant_weight_bit_exact(dev, name, make, ld):
     _assert_same(q, s, q_ref, s_ref, name)
 
 
+@pytest.mark.parametrize("transposed", [False, True], ids=["plain", "transposed"])
 @pytest.mark.parametrize("rule", ["amax", "pow2"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_quant_weight_grouped_bit_exact(dev, dtype, rule):
-    """Several weights in grouped launches: each equal to the oracle's weight quantiser.
+def test_quant_weight_grouped_bit_exact(dev, dtype, rule, transposed):
+    """Several weights in grouped launches: each equal to the oracle's weight quantiser,
+    and with transposed, its transposed copy equal to the oracle's codes and scales
+    transposed (padded rows of the copy untouched).
 
     21 weights (two launches of at most 16): a layer's seven projections at
     reduced size, ragged extents with padded rows, an adversarial weight and
@@ -130,12 +133,25 @@ def test_quant_weight_grouped_bit_exact(dev, dtype, rule):
         ws.append(f(synth.normal((128 * (i + 1), 128), 1.0 + i, 5260 + i)))
         lds.append(128)
     devs = [to_dev(w, ld=ld) for w, ld in zip(ws, lds)]
-    outs = pf.puro_fp8_quant_weight_grouped(devs, pow2=(rule == "pow2"))
+    given, bufs = None, []
+    if transposed:   # transposed copies in buffers with 16 spare codes per row, marked 0x5A
+        given = []
+        for w in ws:
+            r, c = w.shape
+            buf = torch.full((c, (r + 15) // 16 * 16 + 16), 0x5A, dtype=torch.uint8, device="cuda:0")
+            bufs.append((buf, r))
+            given.append((None, None, buf[:, :r], None))
+    outs = pf.puro_fp8_quant_weight_grouped(devs, outs=given, pow2=(rule == "pow2"), transposed=transposed)
     torch.cuda.synchronize()
     assert len(outs) == len(ws) == 21
-    for i, (w, (q, s_)) in enumerate(zip(ws, outs)):
+    for i, (w, o) in enumerate(zip(ws, outs)):
         q_ref, s_ref = oracle.quant_weight(w, rule=rule)
-        _assert_same(q, s_, q_ref, s_ref, "grouped weight %d %s" % (i, w.shape))
+        _assert_same(o[0], o[1], q_ref, s_ref, "grouped weight %d %s" % (i, w.shape))
+        if transposed:
+            _assert_same(o[2], o[3], np.ascontiguousarray(q_ref.T), np.ascontiguousarray(s_ref.T),
+                         "grouped weight %d %s transposed" % (i, w.shape))
+            buf, r = bufs[i]
+            assert (buf[:, r:] == 0x5A).all(), "transposed copy %d wrote past its rows" % i
 
 
 TRANSPOSE_CASES = [
