@@ -994,7 +994,7 @@ hipError_t launch_swiglu_dual(const uint16_t *g, int64_t ldg, const uint16_t *u,
                               bool transpose_out, uint8_t *qt, int64_t ldqt, float *st, bool pow2,
                               hipStream_t stream)
 {
-    const SwigluIn sw{u, ldu, h, ldh};
+    const SwigluIn sw{u, ldu, h, h ? ldh : 0};   // ldh means nothing without h
     return dual_launch(g, true, tokens, cols, ldg, qr, ldqr, sr, transpose_out, qt, ldqt, st, pow2, &sw,
                        stream);
 }
