@@ -1051,26 +1051,6 @@ GemmArgs make_args(const GemmProblem &p)
     return a;
 }
 
-// Estimated time (us) of a whole group on one configuration, with the step
-// times of fast_plan and the group's mean K blocks per tile.
-double group_estimate(int cfg, const std::vector<GemmArgs> &ps)
-{
-    const int TM = cfg == CFG_L ? CfgL::TM : CfgQ::TM, TN = cfg == CFG_L ? CfgL::TN : CfgQ::TN;
-    double tiles = 0.0, steps = 0.0;
-    for (const GemmArgs &a : ps) {
-        const double t = (double)(a.M / TM) * (double)(a.N / TN);
-        tiles += t;
-        int64_t kb = 0;
-        for (int i = 0; i < a.nseg; i++)
-            kb += a.seg[i].KB;
-        steps += t * (double)kb;
-    }
-    const double per_cu = std::ceil(tiles / kComputeUnits), mean = steps / tiles;
-    if (cfg == CFG_L)
-        return per_cu * mean * 4.4 + 5.0;
-    return std::floor(per_cu / 2.0) * mean * 1.9 + std::fmod(per_cu, 2.0) * mean * 1.4;
-}
-
 template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_group_cfg(const std::vector<GemmArgs> &ps, hipStream_t st)
 {
@@ -1107,7 +1087,6 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
     // (longest K first, so that the longest tiles start first); any other
     // non-empty problem runs on its own through the bounds-checked kernel.
     std::vector<GemmArgs> fast;
-    bool all_l = true;
     for (int i = 0; i < count; i++) {
         const GemmProblem &p = probs[i];
         if (p.M == 0 || p.N == 0)
@@ -1117,7 +1096,6 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
             k_aligned = k_aligned && p.seg[j].K % 128 == 0;
         if (k_aligned && p.M % CfgQ::TM == 0 && p.N % CfgQ::TN == 0 && fast_ld_ok(make_args(p))) {
             fast.push_back(make_args(p));
-            all_l = all_l && p.M % CfgL::TM == 0 && p.N % CfgL::TN == 0;
         } else {
             const GemmArgs a = make_args(p);
             const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
