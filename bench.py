@@ -367,6 +367,70 @@ def measure_configs(pf, torch, dev, sp, reps=20, warmup=5):
     return out
 
 
+def _timed(torch, fn, args, reps):
+    """Average event-timed microseconds of fn(*args) on the current stream (3 warm-up calls)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        if fn(*args):
+            raise RuntimeError("C-ABI call failed")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn(*args)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def gemm_side(pf, torch, dev, tokens, sp, reps):
+    """Two GEMM forms outside the step, on the gate/up projections of one layer:
+    segment_sum_accumulate: the data gradient of x_mlp as the sum of two K segments held in
+        separate tensors (dY_gate W_gate + dY_up W_up, NN on the forward's codes), added into an
+        existing BF16 output (C += sum: gradient accumulation over micro-batches);
+    mx_forward: the forward gate/up product (N = 12,288) with power-of-two block scales on the
+        scaled FP8 matrix cores."""
+    import synth
+    L = pf.lib()
+    vp = ctypes.c_void_p
+    T, F, H = tokens, 6144, 2048
+    out = {}
+    # K-segment sum with accumulate-into
+    dys = [synth.device_normal((T, F), 1e-3, 9201 + i, "bf16", dev) for i in range(2)]
+    ws = [synth.device_normal((F, H), 0.02, 9203 + i, "f32", dev) for i in range(2)]
+    qd = [pf.puro_fp8_quant_act(d) for d in dys]
+    qw = [pf.puro_fp8_quant_weight(w) for w in ws]
+    C = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
+    segs = [(F, vp(q.data_ptr()), F, vp(sq.data_ptr()), vp(w.data_ptr()), H, vp(sw_.data_ptr()))
+            for (q, sq), (w, sw_) in zip(qd, qw)]
+    desc = (pf.GemmDesc * 1)(pf.gemm_desc(T, H, segs, vp(C.data_ptr()), H, accumulate=True))
+    args = (pf.LAYOUTS["NN"], pf.BGRAN["128x128"], pf.PURO_BF16, desc, 1, sp)
+    us = _timed(torch, L.puro_fp8_gemm_grouped, args, max(reps, 1) * 5)
+    fl = 2.0 * T * H * 2 * F
+    out["segment_sum_accumulate"] = {"shape": [T, H, 2 * F], "segments": 2, "avg_us": round(us, 2),
+                                     "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1)}
+    log("  segment sum + accumulate [%d x %d, K = 2 x %d] (outside the step): %.1f us, %.0f TFLOP/s"
+        % (T, H, F, us, fl / (us * 1e-6) / 1e12))
+    # power-of-two scales on the scaled matrix cores
+    X = synth.device_normal((T, H), 1.0, 9205, "bf16", dev)
+    W = synth.device_normal((2 * F, H), 0.02, 9206, "f32", dev)
+    qx, sx = pf.puro_fp8_quant_act(X, pow2=True)
+    qw2, sw2 = pf.puro_fp8_quant_weight(W, pow2=True)
+    Y = torch.empty((T, 2 * F), dtype=torch.bfloat16, device=dev)
+    need = L.puro_fp8_gemm_mx_workspace_size(pf.LAYOUTS["NT"], T, 2 * F, H, pf.BGRAN["128x128"])
+    wsb = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = (pf.LAYOUTS["NT"], T, 2 * F, H, vp(qx.data_ptr()), H, vp(sx.data_ptr()), vp(qw2.data_ptr()), H,
+            vp(sw2.data_ptr()), pf.BGRAN["128x128"], vp(Y.data_ptr()), pf.PURO_BF16, 2 * F, vp(wsb.data_ptr()),
+            need, sp)
+    us = _timed(torch, L.puro_fp8_gemm_mx, args, max(reps, 1) * 5)
+    fl = 2.0 * T * 2 * F * H
+    out["mx_forward"] = {"shape": [T, 2 * F, H], "avg_us": round(us, 2), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
+                         "frac_fp8_peak": round(fl / (us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    log("  MX forward [%d x %d x %d] (outside the step): %.1f us, %.0f TFLOP/s"
+        % (T, 2 * F, H, us, fl / (us * 1e-6) / 1e12))
+    return out
+
+
 def cpu_baseline(rows):
     """Time the oracle on a bounded sample of one layer of the same workload."""
     import numpy as np
@@ -541,6 +605,7 @@ def main():
             ("%.0f TFLOP/s" % (v[1] / v[0] / 1e9)) if v[1] else ("%.0f GB/s" % (v[2] / v[0] / 1e6))))
 
     side = {"swiglu_quant_dual": swiglu_side(pf, torch, dev, tokens, sp, args.steps)}
+    side.update(gemm_side(pf, torch, dev, tokens, sp, args.steps))
     del plan, keep
     torch.cuda.empty_cache()
     configs = measure_configs(pf, torch, dev, sp) if not args.no_configs else None
