@@ -384,10 +384,12 @@ def _timed(torch, fn, args, reps):
 
 
 def gemm_side(pf, torch, dev, tokens, sp, reps):
-    """Two GEMM forms outside the step, on the gate/up projections of one layer:
+    """GEMM forms outside the step, on the gate/up projections of one layer:
     segment_sum_accumulate: the data gradient of x_mlp as the sum of two K segments held in
         separate tensors (dY_gate W_gate + dY_up W_up, NN on the forward's codes), added into an
         existing BF16 output (C += sum: gradient accumulation over micro-batches);
+    tn_wgrad: the gate projection's weight gradient (6,144 x 2,048, K = 8,192 tokens) in TN form, on
+        untransposed 128-token copies of dY and X;
     mx_forward: the forward gate/up product (N = 12,288) with power-of-two block scales on the
         scaled FP8 matrix cores."""
     import synth
@@ -411,6 +413,20 @@ def gemm_side(pf, torch, dev, tokens, sp, reps):
                                      "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1)}
     log("  segment sum + accumulate [%d x %d, K = 2 x %d] (outside the step): %.1f us, %.0f TFLOP/s"
         % (T, H, F, us, fl / (us * 1e-6) / 1e12))
+    # weight gradient in TN form, on untransposed 128-token copies (dW_gate = dY_gate^T X)
+    qdt, sdt = pf.puro_fp8_quant_transpose(dys[0], transpose_out=False)
+    Xg = synth.device_normal((T, H), 1.0, 9207, "bf16", dev)
+    qxt, sxt = pf.puro_fp8_quant_transpose(Xg, transpose_out=False)
+    dW = torch.empty((F, H), dtype=torch.float32, device=dev)
+    need = L.puro_fp8_gemm_workspace_size(pf.LAYOUTS["TN"], F, H, T, pf.BGRAN["1x128"])
+    wst = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = (pf.LAYOUTS["TN"], F, H, T, vp(qdt.data_ptr()), F, vp(sdt.data_ptr()), vp(qxt.data_ptr()), H,
+            vp(sxt.data_ptr()), pf.BGRAN["1x128"], vp(dW.data_ptr()), pf.PURO_F32, H, vp(wst.data_ptr()), need, sp)
+    us = _timed(torch, L.puro_fp8_gemm, args, max(reps, 1) * 5)
+    fl = 2.0 * F * H * T
+    out["tn_wgrad"] = {"shape": [F, H, T], "avg_us": round(us, 2), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1)}
+    log("  TN weight gradient [%d x %d, K = %d] (outside the step): %.1f us, %.0f TFLOP/s"
+        % (F, H, T, us, fl / (us * 1e-6) / 1e12))
     # power-of-two scales on the scaled matrix cores
     X = synth.device_normal((T, H), 1.0, 9205, "bf16", dev)
     W = synth.device_normal((2 * F, H), 0.02, 9206, "f32", dev)
