@@ -675,7 +675,9 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     auto run = [&](auto &&stg, int64_t b0, int64_t b1) {
         if (b0 < b1)
             stg(b0, lds0, lds_sc0);
-        if constexpr (Cfg::STATIC_STAGES) {
+        // the scaled-matrix-core form holds no widened fragments: it has the registers for
+        // statically named stages in every configuration
+        if constexpr (Cfg::STATIC_STAGES || MX) {
             for (int64_t kb = b0; kb < b1; kb += 2) {
                 kblock(stg, kb, b1, lds0, lds_sc0, lds1, lds_sc1);
                 if (kb + 1 < b1)
@@ -920,8 +922,6 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K, bool mx = false)
     const int64_t KB = K / 128;
     double best_us = 1e300;
     for (int cfg : {CFG_L, CFG_Q}) {
-        if (mx && cfg != CFG_Q)   // the scaled-matrix-core variant is built for 128 x 128 tiles only
-            continue;
         const int TM = cfg == CFG_L ? CfgL::TM : CfgQ::TM, TN = cfg == CFG_L ? CfgL::TN : CfgQ::TN;
         if (M % TM || N % TN)
             continue;
@@ -931,10 +931,13 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K, bool mx = false)
                 break;
             const double steps = (double)((KB + sp - 1) / sp);
             const int64_t per_cu = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
-            double us = cfg == CFG_L ? (double)per_cu * steps * 4.4 + 5.0
-                                     : (double)(per_cu / 2) * steps * 1.9 + (double)(per_cu % 2) * steps * 1.4;
-            if (mx)   // no widening or promotion: about 0.6 of the step time
-                us *= 0.6;
+            double us;
+            if (!mx)
+                us = cfg == CFG_L ? (double)per_cu * steps * 4.4 + 5.0
+                                  : (double)(per_cu / 2) * steps * 1.9 + (double)(per_cu % 2) * steps * 1.4;
+            else   // scaled matrix cores: no widening or promotion, both tile sizes with static stages
+                us = cfg == CFG_L ? (double)per_cu * (steps * 2.13 + 1.1) + 5.0
+                                  : (double)(per_cu / 2) * (steps * 1.07 + 5.6) + (double)(per_cu % 2) * (steps * 0.8 + 4.0);
             if (sp > 1)
                 us += (double)(sp + 1) * (double)M * (double)N * 4.0 / 4e6 + 5.0;
             if (us < best_us) {
@@ -1003,6 +1006,8 @@ hipError_t launch_mx_t(const GemmArgs &a, float *ws, hipStream_t st)
     const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K, true);
     if (!plan.ok || !fast_ld_ok(a))
         return hipErrorInvalidValue;   // the API layer admits aligned shapes and leading dimensions only
+    if (plan.cfg == CFG_L)
+        return launch_fast_cfg<CfgL, LAYOUT, BGRAN, CBF16, true>(a, plan.splits, ws, st);
     return launch_fast_cfg<CfgQ, LAYOUT, BGRAN, CBF16, true>(a, plan.splits, ws, st);
 }
 

@@ -127,6 +127,29 @@ def test_mx_gemm_within_the_matrix_core_bound(dev, M, N, K, layout, bgran, out):
     assert bad.size == 0, ("element bound", tuple(bad[0]))
 
 
+@pytest.mark.parametrize("bgran", ["1x128", "128x128"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_mx_gemm_large_tiles(dev, layout, bgran):
+    """A product large enough for the 256 x 256 workgroup tiles (4096 x 4096 x 256): 3,000
+    sampled entries, including the four corners, within the same matrix-core bound."""
+    M, N, K = 4096, 4096, 256
+    X = synth.normal((M, K), 1.0, 5401)
+    W = synth.normal((N, K), 0.02, 5402)
+    (qa, sa, qb, sb), dev_ops = _operands(layout, bgran, X, W)
+    C = pf.puro_fp8_gemm(layout, *dev_ops, bgran=bgran, out_dtype=torch.float32, mx=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5403)
+    ms, ns = rng.integers(0, M, 3000), rng.integers(0, N, 3000)
+    ms[:4], ns[:4] = [0, 0, M - 1, M - 1], [0, N - 1, 0, N - 1]
+    ref = oracle.gemm_entries(layout, qa, sa, qb, sb, bgran, ms, ns)
+    c_abs = oracle.gemm_entries(layout, qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), bgran, ms, ns)
+    E = (2.0 ** -9 + (4 * (K // 128) + 4) * 2.0 ** -23) * c_abs
+    got = host(C)[ms, ns].astype(np.float64)
+    bad = np.flatnonzero(np.abs(got - ref) > E)
+    assert bad.size == 0, ("entry", int(ms[bad[0]]), int(ns[bad[0]]), got[bad[0]], ref[bad[0]])
+    assert rel_frobenius(got, ref) <= 1e-3
+
+
 def test_mx_gemm_agrees_with_the_promoting_path(dev):
     # the same power-of-two codes and scales through puro_fp8_gemm (FP32-exact block
     # partials) and puro_fp8_gemm_mx: both within the matrix-core bound of each other
