@@ -295,3 +295,24 @@ def test_quant_weight_grouped_validation(name):
     assert call([D(P, 256, 384, 384, P, 384, P, P, 256, NUL)]) == NULL    # st missing
     assert call([D(NUL, 0, 384, 384, NUL, 384, NUL, P, 0, NUL)]) == OK    # empty weight: nothing
 
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """The header is plain C: a C11 program includes it, links against the library and calls
+    the two calls that need no GPU."""
+    src = tmp_path / "use.c"
+    src.write_text('#include <stdio.h>\n#include <string.h>\n#include "puro_fp8.h"\n'
+                   "int main(void) {\n"
+                   "    puro_quant_weight_desc_t d;\n    puro_gemm_desc_t g;\n"
+                   "    memset(&d, 0, sizeof d);\n    memset(&g, 0, sizeof g);\n"
+                   "    if (puro_fp8_version() != 100) return 1;\n"
+                   "    if (strcmp(puro_status_string(PURO_ERR_SHAPE), puro_status_string(PURO_OK)) == 0) return 2;\n"
+                   "    printf(\"%s\\n\", puro_status_string(PURO_ERR_ALIGN));\n    return 0;\n}\n")
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(pf.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I" + os.path.dirname(HEADER), str(src), "-o", str(exe), "-L" + libdir, "-lpuro_fp8",
+                    "-Wl,-rpath," + libdir], check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == pf.puro_status_string(3)
