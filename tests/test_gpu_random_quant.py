@@ -6,6 +6,8 @@ rule (the recipe's amax / 448 or the power-of-two one) and the value
 distribution (normal, lognormal with zero blocks, or outlier channels), and runs
 every quantiser entry point on the same input.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +20,8 @@ from helpers import first_mismatch, host, to_dev
 pytestmark = pytest.mark.gpu
 
 EXTENTS = [1, 5, 16, 127, 128, 129, 200, 256, 300, 384, 640]
+# number of seeded cases (a wider sweep: set PURO_RANDOM_CASES, e.g. 400)
+CASES = int(os.environ.get("PURO_RANDOM_CASES", "24"))
 
 
 def _same(t, ref, what):
@@ -43,7 +47,7 @@ def _input(rng, rows, cols, seed):
     return x
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(CASES))
 def test_random_quantisers(dev, seed):
     rng = np.random.default_rng(9100 + seed)
     rows, cols = int(rng.choice(EXTENTS)), int(rng.choice(EXTENTS))

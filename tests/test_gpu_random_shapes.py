@@ -8,6 +8,8 @@ from the oracle's and the library's quantisers (byte-compared first); products
 are held to the bounds of the fixed-shape tests (FP32: 2e-6 relative Frobenius
 and the per-element accumulation bound; BF16: that bound plus one rounding).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +23,8 @@ pytestmark = pytest.mark.gpu
 
 EXTENTS = [1, 7, 64, 127, 128, 129, 200, 256, 383, 384, 512, 640]
 KS = [1, 100, 128, 129, 255, 256, 384, 1000, 1024, 2048]
+# number of seeded cases (a wider sweep: set PURO_RANDOM_CASES, e.g. 400)
+CASES = int(os.environ.get("PURO_RANDOM_CASES", "24"))
 
 
 def _case(seed):
@@ -33,7 +37,7 @@ def _case(seed):
     return layout, bgran, out, M, N, K, pad
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(CASES))
 def test_random_gemm(dev, seed):
     layout, bgran, out, M, N, K, pad = _case(8100 + seed)
     X = synth.normal((M, K), 1.0, 8200 + seed)
@@ -43,7 +47,7 @@ def test_random_gemm(dev, seed):
     _check_product(layout, bgran, hostops, devops, out)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(max(1, CASES // 3)))
 def test_random_grouped(dev, seed):
     """1-5 NT problems in one grouped call, 1-3 K segments each, some adding into C."""
     rng = np.random.default_rng(8400 + seed)
