@@ -14,11 +14,16 @@ Names mirror the C entry points:
     puro_fp8_swiglu_quant_dual(gate, up)  -> h = bf16(silu(gate) * up) and its dual quantisation
     puro_fp8_gemm(layout, A, sA, B, sB, bgran, out_dtype) -> C
     puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
+    puro_fp8_gemm(..., mx=True)           -> puro_fp8_gemm_mx (power-of-two scales, scaled matrix cores)
+    puro_fp8_gemm(..., native=True)       -> puro_fp8_gemm_native (partials on the FP8 matrix cores)
     puro_status_string(status)
 Tensors are 2-D, row-major (stride(1) == 1), with a row stride that is a
 multiple of 16 elements and 16-byte aligned storage.
 """
+import contextlib
 import ctypes
+import functools
+import inspect
 import os
 
 import torch
@@ -101,12 +106,14 @@ def lib():
             f.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, vp, i64, vp, i32, vp, i64, vp, vp]
         L.puro_fp8_gemm_workspace_size.restype = ctypes.c_size_t
         L.puro_fp8_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i32]
-        for name in ("puro_fp8_gemm", "puro_fp8_gemm_mx"):
+        for name in ("puro_fp8_gemm", "puro_fp8_gemm_mx", "puro_fp8_gemm_native"):
             f = getattr(L, name)
             f.restype = i32
             f.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp, ctypes.c_size_t, vp]
-        L.puro_fp8_gemm_mx_workspace_size.restype = ctypes.c_size_t
-        L.puro_fp8_gemm_mx_workspace_size.argtypes = [i32, i64, i64, i64, i32]
+        for name in ("puro_fp8_gemm_mx_workspace_size", "puro_fp8_gemm_native_workspace_size"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_size_t
+            f.argtypes = [i32, i64, i64, i64, i32]
         for name in ("puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2"):
             f = getattr(L, name)
             f.restype = i32
@@ -133,6 +140,21 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _on(stream):
+    """Context in which the wrappers allocate: the launch stream.
+
+    Outputs and the split-K workspace allocated here belong to the stream the
+    kernels run on, so PyTorch's caching allocator hands their memory to later
+    work on that stream only after the kernels (stream order).  Allocating on
+    another current stream would let that stream reuse the workspace while the
+    kernels still write it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
 
 
 def _ptr(t):
@@ -185,12 +207,25 @@ def _need(t, shape, dtype, name):
             name, tuple(shape), dtype, tuple(t.shape), t.dtype))
 
 
+def _stream_allocs(fn):
+    """Runs the wrapper with its allocations on the launch stream (see _on)."""
+    pos = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def run(*args, **kw):
+        stream = args[pos] if len(args) > pos else kw.get("stream")
+        with _on(stream):
+            return fn(*args, **kw)
+    return run
+
+
 def _need_dense(t, shape, name):
     _need(t, shape, torch.float32, name)
     if not t.is_contiguous():
         raise ValueError("%s: scale arrays must be dense (contiguous)" % name)
 
 
+@_stream_allocs
 def puro_fp8_quant_act(x, q=None, s=None, stream=None, pow2=False):
     """1x128 blocks along each row of x [rows][cols] (float32 / bfloat16).
     pow2: power-of-two block scales (puro_fp8_quant_act_pow2)."""
@@ -207,6 +242,7 @@ def puro_fp8_quant_act(x, q=None, s=None, stream=None, pow2=False):
     return q, s
 
 
+@_stream_allocs
 def puro_fp8_quant_weight(w, q=None, s=None, stream=None, pow2=False):
     """128x128 tiles of w [rows][cols] (float32 / bfloat16); pow2: power-of-two scales."""
     rows, cols = w.shape
@@ -222,6 +258,7 @@ def puro_fp8_quant_weight(w, q=None, s=None, stream=None, pow2=False):
     return q, s
 
 
+@_stream_allocs
 def puro_fp8_quant_weight_grouped(weights, outs=None, stream=None, pow2=False, transposed=False):
     """128x128 tiles of several weights (one dtype) in as few launches as possible.
 
@@ -268,6 +305,7 @@ def puro_fp8_quant_weight_grouped(weights, outs=None, stream=None, pow2=False, t
     return res
 
 
+@_stream_allocs
 def puro_fp8_quant_transpose(x, transpose_out=True, q=None, s=None, stream=None, pow2=False):
     """128-token blocks per column of x [tokens][cols].
 
@@ -307,6 +345,7 @@ def _dual_outs(tokens, cols, transpose_out, device, q_row, s_row, q_tok, s_tok):
     return q_row, s_row, q_tok, s_tok
 
 
+@_stream_allocs
 def puro_fp8_quant_dual(x, transpose_out=True, q_row=None, s_row=None, q_tok=None, s_tok=None,
                         stream=None, pow2=False):
     """One read of x [tokens][cols]: the outputs of puro_fp8_quant_act(x) and of
@@ -320,6 +359,7 @@ def puro_fp8_quant_dual(x, transpose_out=True, q_row=None, s_row=None, q_tok=Non
     return q_row, s_row, q_tok, s_tok
 
 
+@_stream_allocs
 def puro_fp8_swiglu_quant_dual(gate, up, transpose_out=True, h=None, store_h=True, q_row=None, s_row=None,
                                q_tok=None, s_tok=None, stream=None, pow2=False):
     """h = bf16(silu(gate) * up) for bfloat16 gate, up [tokens][cols], quantised as
@@ -380,11 +420,20 @@ def puro_fp8_gemm_mx_workspace_size(layout, M, N, K, bgran):
     return int(lib().puro_fp8_gemm_mx_workspace_size(LAYOUTS[layout], M, N, K, BGRAN[bgran]))
 
 
+def puro_fp8_gemm_native_workspace_size(layout, M, N, K, bgran):
+    return int(lib().puro_fp8_gemm_native_workspace_size(LAYOUTS[layout], M, N, K, BGRAN[bgran]))
+
+
+@_stream_allocs
 def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat16, C=None,
-                  workspace=None, stream=None, mx=False):
+                  workspace=None, stream=None, mx=False, native=False):
     """Blockwise-scaled E4M3 GEMM; returns C [M][N] (float32 or bfloat16).
     mx: the scaled-FP8-matrix-core variant (puro_fp8_gemm_mx: power-of-two scales,
-    extents multiples of 128)."""
+    extents multiples of 128).  native: block partials on the native FP8 matrix
+    cores (puro_fp8_gemm_native: amax/448 scales, extents multiples of 128, not
+    FP32-exact per block)."""
+    if mx and native:
+        raise ValueError("mx and native are different entry points")
     M, N, K = gemm_dims(layout, A, B)
     if A.dtype != torch.uint8 or B.dtype != torch.uint8:
         raise TypeError("A and B hold E4M3 codes (torch.uint8)")
@@ -396,14 +445,16 @@ def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat1
     if C is None:
         C = empty_2d(M, N, out_dtype, A.device)
     _need(C, (M, N), out_dtype, "C")
-    need = (puro_fp8_gemm_mx_workspace_size if mx else puro_fp8_gemm_workspace_size)(layout, M, N, K, bgran)
+    size_fn = (puro_fp8_gemm_mx_workspace_size if mx else
+               puro_fp8_gemm_native_workspace_size if native else puro_fp8_gemm_workspace_size)
+    need = size_fn(layout, M, N, K, bgran)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
-    fn = lib().puro_fp8_gemm_mx if mx else lib().puro_fp8_gemm
-    _check(fn(LAYOUTS[layout], M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB), BGRAN[bgran],
-              _ptr(C), PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32, _ld(C), _ptr(workspace),
-              ws_bytes, _stream(stream)), "puro_fp8_gemm_mx" if mx else "puro_fp8_gemm")
+    name = "puro_fp8_gemm_mx" if mx else "puro_fp8_gemm_native" if native else "puro_fp8_gemm"
+    _check(getattr(lib(), name)(LAYOUTS[layout], M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB),
+                                BGRAN[bgran], _ptr(C), PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32,
+                                _ld(C), _ptr(workspace), ws_bytes, _stream(stream)), name)
     return C
 
 
@@ -446,6 +497,7 @@ def gemm_descs(layout, problems, bgran="128x128", out_dtype=torch.bfloat16):
     return descs, outs
 
 
+@_stream_allocs
 def puro_fp8_gemm_grouped(layout, problems, bgran="128x128", out_dtype=torch.bfloat16, stream=None):
     """Independent blockwise-scaled E4M3 GEMMs sharing layout, B-scale
     granularity and output dtype, in as few launches as possible.

@@ -411,6 +411,43 @@ puro_status_t puro_fp8_gemm_mx(puro_layout_t layout, int64_t M, int64_t N, int64
     }
 }
 
+size_t puro_fp8_gemm_native_workspace_size(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                                           puro_bscale_t bgran)
+{
+    if (layout != PURO_NT && layout != PURO_NN && layout != PURO_TN)
+        return 0;
+    if (bgran != PURO_SCALE_1x128 && bgran != PURO_SCALE_128x128)
+        return 0;
+    if (bad_extent(M) || bad_extent(N) || bad_extent(K) || !mx_aligned(M, N, K))
+        return 0;
+    puro::GemmProblem p = make_problem(layout, M, N, K, nullptr, 0, nullptr, nullptr, 0, nullptr, bgran, nullptr,
+                                       PURO_F32, N);
+    return puro::gemm_native_workspace_bytes(p);
+}
+
+puro_status_t puro_fp8_gemm_native(puro_layout_t layout, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                                   int64_t lda, const float *sA, const uint8_t *B, int64_t ldb, const float *sB,
+                                   puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc, void *workspace,
+                                   size_t ws_bytes, hipStream_t stream)
+{
+    try {
+        puro_status_t st = check_gemm(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
+        if (st != PURO_OK)
+            return st;
+        if (M == 0 || N == 0)
+            return PURO_OK;
+        if (!mx_aligned(M, N, K) || lda >= ((int64_t)1 << 28) || ldb >= ((int64_t)1 << 28))
+            return PURO_ERR_SHAPE;
+        puro::GemmProblem p = make_problem(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
+        const size_t need = puro::gemm_native_workspace_bytes(p);
+        if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 256)))
+            return PURO_ERR_WORKSPACE;
+        return from_hip(puro::launch_gemm_native(p, workspace, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
 puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
                                     const puro_gemm_desc_t *problems, int count, hipStream_t stream)
 {

@@ -10,16 +10,23 @@
 // needed), with the per-block promotion of the DeepSeek-V3 design the
 // technical report's related-work paragraph cites.
 //
-// Two matrix-core datapaths form P_kb from the same E4M3 fragments:
-//  * F16 (default): each E4M3 code is widened to FP16 in registers
+// Three matrix-core datapaths, each behind its own entry point:
+//  * F16 (puro_fp8_gemm): each E4M3 code is widened to FP16 in registers
 //    (v_cvt_scalef32_pk_f16_fp8, exact: every E4M3 value is an FP16 value) and
 //    P_kb is four chained v_mfma_f32_16x16x32_f16.  Measured on gfx950, these
 //    sums are FP32-grade (relative error ~1e-8 on quantised data).
-//  * FP8 (native): one v_mfma_f32_16x16x128_f8f6f4.  Twice the peak rate, but
-//    measured on gfx950 it adds each run of 8 consecutive products in a
-//    fixed-point window about 13 bits below the largest of them, so small
-//    products next to large ones are truncated (relative error ~1e-5 to 1e-4
-//    on quantised data).
+//  * FP8 (puro_fp8_gemm_native): one v_mfma_f32_16x16x128_f8f6f4 per block,
+//    promoted the same way.  Twice the peak rate, but measured on gfx950 the
+//    instruction adds each run of 8 consecutive products in a fixed-point
+//    window about 13 bits below the largest of them, so small products next
+//    to large ones are truncated (relative error ~1e-5 to 1e-4 on quantised
+//    data).
+//  * MX (puro_fp8_gemm_mx): power-of-two block scales applied inside
+//    v_mfma_scale_f32_16x16x128_f8f6f4 as E8M0 exponents; no promotion step.
+//
+// Tiles: 128 x 128 per workgroup (4 waves of 64 x 64, two workgroups per CU)
+// or 256 x 256 (8 waves of 128 x 64, one per CU), picked per problem by a
+// host-side cost model from step times measured on gfx950.
 //
 // Register layouts, measured on gfx950: for v_mfma_f32_16x16x128_f8f6f4 lane l
 // holds A row l%16 and B column l%16, bytes 0..31 being K slots
@@ -146,20 +153,18 @@ __device__ __forceinline__ v8h widen8(const v8i &f, int c)
     return r;
 }
 
-// Sum over one 128-wide K block of a(m,k) b(k,n) for a 16x16 output tile.
-template <bool NATIVE_FP8>
+// Sum over one 128-wide K block of a(m,k) b(k,n) for a 16x16 output tile, on
+// the FP16 matrix cores (four chained v_mfma_f32_16x16x32_f16).
 __device__ __forceinline__ v4f block_partial(const v8i &a, const v8i &b)
 {
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (NATIVE_FP8)
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
     v4f p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 0), widen8(b, 0), zero, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 1), widen8(b, 1), p, 0, 0, 0);
     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 2), widen8(b, 2), p, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(widen8(a, 3), widen8(b, 3), p, 0, 0, 0);
 }
 
-template <int LAYOUT, int BGRAN, bool CBF16, bool NATIVE_FP8>
+template <int LAYOUT, int BGRAN, bool CBF16>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
 {
     constexpr bool A_KMAJ = (LAYOUT != 2);
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
         for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const v4f P = block_partial<NATIVE_FP8>(af[i], bf[j]);
+                const v4f P = block_partial(af[i], bf[j]);
 #pragma unroll
                 for (int r = 0; r < 4; r++)
                     acc[i][j][r] = fmaf(sa[i][r] * sb[j], P[r], acc[i][j][r]);
@@ -429,9 +434,12 @@ struct FastCfg {
     static constexpr int LOADS = TM / 8 / NW + TN / 8 / NW + 1;
     // K loop unrolled by the two stages, so that each stage is addressed by a
     // compile-time name: the compiler then sees that the copies into one stage
-    // do not touch the other and lets the copies overlap the reads.  Costs
-    // registers, which the 256 x 256 tile does not have to spare.
-    static constexpr bool STATIC_STAGES = NW <= 4;
+    // do not touch the other and lets the copies overlap the reads.
+    static constexpr bool STATIC_STAGES = true;
+    // Stage unconditionally (an idle copy after the last block): the 8-wave
+    // tile has no registers for the partials of two blocks at once, which
+    // is what the compiler builds when a branch separates them.
+    static constexpr bool IDLE_COPY = NW > 4;
 };
 
 // 256 x 256 workgroup tiles (8 waves of 128 x 64, two LDS stages, one
@@ -465,12 +473,21 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n)
     return (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3);
 }
 
+// Matrix-core datapaths of the tile kernels.
+//  DP_F16: E4M3 widened to FP16, block partials on FP16 matrix cores
+//          (FP32-grade sums), promoted with one FMA per element.
+//  DP_MX:  power-of-two scales applied by the scaled FP8 matrix cores as
+//          E8M0 exponents; no promotion step.
+//  DP_FP8: block partials on the FP8 matrix cores as they are, promoted with
+//          one FMA per element; the instruction's own accumulation of each
+//          run of products is not FP32-exact.
+enum { DP_F16 = 0, DP_MX = 1, DP_FP8 = 2 };
+
 // One workgroup's output tile: rows [m0, m0 + TM) x columns [n0, n0 + TN) of
 // problem p, over K blocks [kb_lo, kb_hi) numbered across its segments.  With
 // OUT_PARTIAL the FP32 result goes to ws[split][M][N] (row stride N) instead
-// of C.  MULTI: p may have more than one segment.  MX: the scales are powers
-// of two and the scaled FP8 matrix cores apply them (see the MX variant).
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, bool MULTI, bool MX = false>
+// of C.  MULTI: p may have more than one segment.  DP: the datapath above.
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, bool MULTI, int DP = DP_F16>
 __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t n0, int64_t kb_lo,
                                           int64_t kb_hi, int split, float *ws)
 {
@@ -490,6 +507,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     __shared__ __attribute__((aligned(16))) float lds_sc0[NW * 64];
     __shared__ __attribute__((aligned(16))) float lds_sc1[NW * 64];
     static_assert(TM + TN <= NW * 64, "one scale slot per lane");
+    constexpr bool MX = DP == DP_MX;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave-level addresses scalar
@@ -564,8 +582,15 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                       float *LSCN) {
         __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of block kb have landed
         __syncthreads();   // everyone's have; block kb-1 (in LN) is no longer read
-        if (kb + 1 < end)
+        if constexpr (Cfg::IDLE_COPY) {
+            // the next block, or block kb again after the last one (into an
+            // idle stage, never read): no branch in the K loop, so the
+            // compiler cannot move a block's promotion past the next block's
+            // staging (which keeps every block's partials live at once)
+            stg(kb + 1 < end ? kb + 1 : kb, LN, LSCN);
+        } else if (kb + 1 < end) {
             stg(kb + 1, LN, LSCN);
+        }
 
         const uint8_t *ta = L;
         const uint8_t *tb = L + A_BYTES;
@@ -595,6 +620,32 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
 #pragma unroll
                     for (int r = 0; r < 4; r++)
                         acc[i][j][r] = c[r];
+                }
+            }
+        } else if constexpr (DP == DP_FP8) {
+            // Native FP8 matrix cores: one v_mfma_f32_16x16x128_f8f6f4 per 16x16
+            // tile and K block (zero scale operands select the unscaled
+            // instruction), promoted like the F16 path.
+            static_assert(!BGRAN || 128 % (JT * 16) == 0, "wave columns within one weight tile");
+            float sbv[JT];
+            v8i bf[JT];
+#pragma unroll
+            for (int j = 0; j < JT; j++) {
+                sbv[j] = BGRAN ? LSC[TM + (wcol >> 7)] : LSC[TM + wcol + j * 16 + (lane & 15)];
+                bf[j] = B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane) : fast_frag_mn<TN>(tb, wcol + j * 16, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < IT; i++) {
+                const v8i af = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
+                const float4 sa4 = *reinterpret_cast<const float4 *>(&LSC[wrow + i * 16 + 4 * (lane >> 4)]);
+                const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+#pragma unroll
+                for (int j = 0; j < JT; j++) {
+                    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[i][j][r] = fmaf(sa[r] * sbv[j], P[r], acc[i][j][r]);
                 }
             }
         } else {
@@ -677,12 +728,16 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             stg(b0, lds0, lds_sc0);
         // the scaled-matrix-core form holds no widened fragments: it has the registers for
         // statically named stages in every configuration
-        if constexpr (Cfg::STATIC_STAGES || MX) {
-            for (int64_t kb = b0; kb < b1; kb += 2) {
+        if constexpr (Cfg::STATIC_STAGES || DP != DP_F16) {
+            // pairs of blocks, then an odd last block: no compute is
+            // conditional inside the loop
+            int64_t kb = b0;
+            for (; kb + 2 <= b1; kb += 2) {
                 kblock(stg, kb, b1, lds0, lds_sc0, lds1, lds_sc1);
-                if (kb + 1 < b1)
-                    kblock(stg, kb + 1, b1, lds1, lds_sc1, lds0, lds_sc0);
+                kblock(stg, kb + 1, b1, lds1, lds_sc1, lds0, lds_sc0);
             }
+            if (kb < b1)
+                kblock(stg, kb, b1, lds0, lds_sc0, lds1, lds_sc1);
         } else {
             // stage chosen at run time: every read of a stage waits for the copies in flight
             for (int64_t kb = b0; kb < b1; kb++) {
@@ -713,8 +768,10 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             int64_t step;
             scale_source(sg, scb, step);
             auto stg = [&](int64_t kb, uint8_t *L, float *LSC) { stage_seg(sg, kb, scb + kb * step, L, LSC); };
-            if (si > 0)
+            if (si > 0) {
+                __builtin_amdgcn_s_waitcnt(0);   // the previous run's copies have all landed
                 __syncthreads();
+            }
             run(stg, 0, sg.KB);
         }
     }
@@ -730,6 +787,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
     constexpr int NCH = 16 * CW / CH;                        // 16-byte chunks per strip
     static_assert(NCH % 64 == 0, "whole chunks per lane");
     static_assert(16 * SST * 4 * NW <= A_BYTES + B_BYTES, "strips fit in one stage");
+    __builtin_amdgcn_s_waitcnt(0);   // no copy is in flight (the idle copy of IDLE_COPY)
     __syncthreads();   // every wave is done with the last K block: stage 0 is free
     float *strip = reinterpret_cast<float *>(lds0) + wave * 16 * SST;
     const int wrow = wm * IT * 16, wcol = wn * JT * 16;
@@ -815,7 +873,7 @@ __device__ __forceinline__ GemmArgs load_args(KernargGemm src)
     return a;
 }
 
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, bool MX = false>
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool OUT_PARTIAL, int DP = DP_F16>
 __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs args, int tiles_m, int tiles_n,
                                                                  int splits, float *ws)
 {
@@ -829,7 +887,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs arg
     // split K only for single-segment products
     const int64_t KB = p.seg[0].KB;
     const int64_t kb_lo = KB * split / splits, kb_hi = KB * (split + 1) / splits;
-    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, OUT_PARTIAL, false, MX>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN,
+    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, OUT_PARTIAL, false, DP>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN,
                                                              kb_lo, kb_hi, split, ws);
 }
 
@@ -842,7 +900,7 @@ struct GroupArgs {
     int count;
 };
 
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool MULTI>
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool MULTI, int DP = DP_F16>
 __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_group_kernel(GroupArgs args)
 {
     (void)args;   // read through the argument segment pointer below
@@ -866,8 +924,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_group_kernel(GroupArgs a
     for (int s = 0; s < kMaxKSeg; s++)
         if (s < p.nseg)
             blocks += p.seg[s].KB;
-    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, false, MULTI>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN, 0, blocks,
-                                                       0, nullptr);
+    fast_tile<Cfg, LAYOUT, BGRAN, CBF16, false, MULTI, DP>(p, (int64_t)tm * Cfg::TM, (int64_t)tn * Cfg::TN, 0, blocks,
+                                                           0, nullptr);
 }
 
 // C[m][n] = sum over s = 0 .. splits-1, in that order, of ws[s][m][n]; four
@@ -907,37 +965,59 @@ struct FastPlan {
 
 constexpr int kComputeUnits = 256;
 
-// Picks the candidate with the least estimated time.  The estimate uses
-// per-K-block step times measured on gfx950 with every CU busy: a 256 x 256
-// tile (one workgroup per CU) takes about 4.4 us per K block; a 128 x 128 tile
-// about 1.9 us when two share a CU and 1.4 us alone.  Workgroups are spread
-// evenly over the CUs, so the busiest CU sets the time.  Splitting K adds
-// the partial sums, (splits + 1) M N 4 bytes moved at about 4 TB/s, and the
-// reduction launch.
-FastPlan fast_plan(int64_t M, int64_t N, int64_t K, bool mx = false)
+// Per-tile cost of a tile configuration on one datapath, measured on gfx950
+// with every CU busy (us): a tile takes `fixed + blocks * step`; 128 x 128
+// tiles run two per CU (`step2`, `fixed2` each pair) and `step1`, `fixed1`
+// when one is left alone.
+struct TileCost {
+    double step2, fixed2, step1, fixed1;
+};
+
+TileCost tile_cost(int cfg, int dp)
+{
+    if (cfg == CFG_Q) {
+        if (dp == DP_F16)
+            return {1.96, 4.1, 1.4, 3.0};
+        if (dp == DP_MX)
+            return {1.07, 5.6, 0.8, 4.0};
+        return {1.24, 2.2, 0.9, 2.0};
+    }
+    if (dp == DP_F16)
+        return {3.6, 13.4, 3.6, 13.4};
+    if (dp == DP_MX)
+        return {2.13, 6.1, 2.13, 6.1};
+    return {2.24, 6.1, 2.24, 6.1};
+}
+
+// Picks the candidate with the least estimated time.  Workgroups are spread
+// evenly over the CUs, so the busiest CU sets the time.  Splitting K adds the
+// partial sums, (splits + 1) M N 4 bytes moved at about 4 TB/s, and the
+// reduction launch.  On the FP32-exact datapath the 256 x 256 tile is
+// considered for NT products with 128x128 B scales only, the one case where
+// it measured faster.
+FastPlan fast_plan(int64_t M, int64_t N, int64_t K, int dp, bool nt, bool bgran128)
 {
     FastPlan best = {false, CFG_Q, 1};
     if (K <= 0 || K % 128 || M % CfgQ::TM || N % CfgQ::TN)
         return best;
     const int64_t KB = K / 128;
     double best_us = 1e300;
-    for (int cfg : {CFG_L, CFG_Q}) {
-        const int TM = cfg == CFG_L ? CfgL::TM : CfgQ::TM, TN = cfg == CFG_L ? CfgL::TN : CfgQ::TN;
-        if (M % TM || N % TN)
+    for (int cfg : {(int)CFG_L, (int)CFG_Q}) {
+        if (cfg == CFG_L && dp == DP_F16 && !(nt && bgran128))
             continue;
-        const int64_t tiles = (M / TM) * (N / TN);
+        const int T = cfg == CFG_Q ? CfgQ::TM : CfgL::TM;
+        if (M % T || N % T)
+            continue;
+        const TileCost c = tile_cost(cfg, dp);
+        const int64_t tiles = (M / T) * (N / T);
         for (int sp = 1; sp <= 8; sp *= 2) {
             if (sp > 1 && KB / sp < 4)
                 break;
             const double steps = (double)((KB + sp - 1) / sp);
             const int64_t per_cu = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
-            double us;
-            if (!mx)
-                us = cfg == CFG_L ? (double)per_cu * steps * 4.4 + 5.0
-                                  : (double)(per_cu / 2) * steps * 1.9 + (double)(per_cu % 2) * steps * 1.4;
-            else   // scaled matrix cores: no widening or promotion, both tile sizes with static stages
-                us = cfg == CFG_L ? (double)per_cu * (steps * 2.13 + 1.1) + 5.0
-                                  : (double)(per_cu / 2) * (steps * 1.07 + 5.6) + (double)(per_cu % 2) * (steps * 0.8 + 4.0);
+            double us = cfg == CFG_Q ? (double)(per_cu / 2) * (steps * c.step2 + c.fixed2) +
+                                           (double)(per_cu % 2) * (steps * c.step1 + c.fixed1)
+                                     : (double)per_cu * (steps * c.step1 + c.fixed1);
             if (sp > 1)
                 us += (double)(sp + 1) * (double)M * (double)N * 4.0 / 4e6 + 5.0;
             if (us < best_us) {
@@ -949,17 +1029,17 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K, bool mx = false)
     return best;
 }
 
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool MX = false>
+template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, int DP>
 hipError_t launch_fast_cfg(const GemmArgs &a, int splits, float *ws, hipStream_t st)
 {
     const int tiles_m = (int)(a.M / Cfg::TM), tiles_n = (int)(a.N / Cfg::TN);
     const dim3 grid((unsigned)(tiles_m * tiles_n * splits));
     if (splits == 1) {
-        hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, false, MX>), grid, dim3(Cfg::THREADS), 0,
+        hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, false, DP>), grid, dim3(Cfg::THREADS), 0,
                            st, a, tiles_m, tiles_n, 1, (float *)nullptr);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, true, MX>), grid, dim3(Cfg::THREADS), 0, st,
+    hipLaunchKernelGGL((gemm_fast_kernel<Cfg, LAYOUT, BGRAN, CBF16, true, DP>), grid, dim3(Cfg::THREADS), 0, st,
                        a, tiles_m, tiles_n, splits, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -970,7 +1050,7 @@ hipError_t launch_fast_cfg(const GemmArgs &a, int splits, float *ws, hipStream_t
     return hipGetLastError();
 }
 
-// The tile kernel's copies take a 32-bit per-lane offset of up to 7 leading
+// The tile kernels' copies take a 32-bit per-lane offset of up to 7 leading
 // dimensions: every segment's leading dimensions must be below 2^28.
 constexpr int64_t kFastLdLimit = (int64_t)1 << 28;
 bool fast_ld_ok(const GemmArgs &a)
@@ -981,42 +1061,48 @@ bool fast_ld_ok(const GemmArgs &a)
     return ok;
 }
 
-template <int LAYOUT, int BGRAN, bool CBF16>
-hipError_t launch_fast(const GemmArgs &a, const FastPlan &plan, float *ws, hipStream_t st)
+template <int LAYOUT, int BGRAN, bool CBF16, int DP>
+hipError_t launch_planned(const GemmArgs &a, const FastPlan &plan, float *ws, hipStream_t st)
 {
-    if (plan.cfg == CFG_L)
-        return launch_fast_cfg<CfgL, LAYOUT, BGRAN, CBF16>(a, plan.splits, ws, st);
-    return launch_fast_cfg<CfgQ, LAYOUT, BGRAN, CBF16>(a, plan.splits, ws, st);
+    if (plan.cfg == CFG_L) {
+        // the FP32-exact datapath plans 256 x 256 tiles for NT with 128x128 B scales only
+        if constexpr (DP != DP_F16 || (LAYOUT == 0 && BGRAN == 1))
+            return launch_fast_cfg<CfgL, LAYOUT, BGRAN, CBF16, DP>(a, plan.splits, ws, st);
+        return hipErrorInvalidValue;
+    }
+    return launch_fast_cfg<CfgQ, LAYOUT, BGRAN, CBF16, DP>(a, plan.splits, ws, st);
 }
 
+// FP32-exact datapath: aligned shapes take the tile kernels, any other the
+// bounds-checked general kernel.
 template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_one(const GemmArgs &a, float *ws, hipStream_t st)
 {
-    const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K);
+    const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K, DP_F16, LAYOUT == 0, BGRAN == 1);
     if (plan.ok && fast_ld_ok(a))
-        return launch_fast<LAYOUT, BGRAN, CBF16>(a, plan, ws, st);
+        return launch_planned<LAYOUT, BGRAN, CBF16, DP_F16>(a, plan, ws, st);
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
-template <int LAYOUT, int BGRAN, bool CBF16>
-hipError_t launch_mx_t(const GemmArgs &a, float *ws, hipStream_t st)
+// Scaled (MX) and native FP8 datapaths: aligned shapes only (the API layer
+// admits no others).
+template <int LAYOUT, int BGRAN, bool CBF16, int DP>
+hipError_t launch_aligned_t(const GemmArgs &a, float *ws, hipStream_t st)
 {
-    const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K, true);
+    const FastPlan plan = fast_plan(a.M, a.N, a.seg[0].K, DP, LAYOUT == 0, BGRAN == 1);
     if (!plan.ok || !fast_ld_ok(a))
-        return hipErrorInvalidValue;   // the API layer admits aligned shapes and leading dimensions only
-    if (plan.cfg == CFG_L)
-        return launch_fast_cfg<CfgL, LAYOUT, BGRAN, CBF16, true>(a, plan.splits, ws, st);
-    return launch_fast_cfg<CfgQ, LAYOUT, BGRAN, CBF16, true>(a, plan.splits, ws, st);
+        return hipErrorInvalidValue;
+    return launch_planned<LAYOUT, BGRAN, CBF16, DP>(a, plan, ws, st);
 }
 
-template <int LAYOUT>
-hipError_t launch_mx_layout(const GemmProblem &p, const GemmArgs &a, float *ws, hipStream_t st)
+template <int LAYOUT, int DP>
+hipError_t launch_aligned_layout(const GemmProblem &p, const GemmArgs &a, float *ws, hipStream_t st)
 {
     if (p.bgran)
-        return p.c_bf16 ? launch_mx_t<LAYOUT, 1, true>(a, ws, st) : launch_mx_t<LAYOUT, 1, false>(a, ws, st);
-    return p.c_bf16 ? launch_mx_t<LAYOUT, 0, true>(a, ws, st) : launch_mx_t<LAYOUT, 0, false>(a, ws, st);
+        return p.c_bf16 ? launch_aligned_t<LAYOUT, 1, true, DP>(a, ws, st) : launch_aligned_t<LAYOUT, 1, false, DP>(a, ws, st);
+    return p.c_bf16 ? launch_aligned_t<LAYOUT, 0, true, DP>(a, ws, st) : launch_aligned_t<LAYOUT, 0, false, DP>(a, ws, st);
 }
 
 template <int LAYOUT>
@@ -1056,8 +1142,10 @@ GemmArgs make_args(const GemmProblem &p)
     return a;
 }
 
-template <class Cfg, int LAYOUT, int BGRAN, bool CBF16>
-hipError_t launch_group_cfg(const std::vector<GemmArgs> &ps, hipStream_t st)
+// One or more grouped launches of problems sharing a tile size: T = 128 or
+// 256 (fast_tile's two configurations).
+template <int T, int LAYOUT, int BGRAN, bool CBF16>
+hipError_t launch_group_tiles(const std::vector<GemmArgs> &ps, hipStream_t st)
 {
     for (size_t lo = 0; lo < ps.size(); lo += kGroupMax) {
         GroupArgs g;
@@ -1065,25 +1153,42 @@ hipError_t launch_group_cfg(const std::vector<GemmArgs> &ps, hipStream_t st)
         g.first[0] = 0;
         for (int i = 0; i < g.count; i++) {
             g.p[i] = ps[lo + i];
-            g.first[i + 1] = g.first[i] + (int)((g.p[i].M / Cfg::TM) * (g.p[i].N / Cfg::TN));
+            g.first[i + 1] = g.first[i] + (int)((g.p[i].M / T) * (g.p[i].N / T));
         }
         // launches whose problems all have one K segment take the kernel
         // without the segment lookup
         bool multi = false;
         for (int i = 0; i < g.count; i++)
             multi = multi || g.p[i].nseg > 1;
-        if (multi)
-            hipLaunchKernelGGL((gemm_group_kernel<Cfg, LAYOUT, BGRAN, CBF16, true>),
-                               dim3((unsigned)g.first[g.count]), dim3(Cfg::THREADS), 0, st, g);
-        else
-            hipLaunchKernelGGL((gemm_group_kernel<Cfg, LAYOUT, BGRAN, CBF16, false>),
-                               dim3((unsigned)g.first[g.count]), dim3(Cfg::THREADS), 0, st, g);
+        const dim3 grid((unsigned)g.first[g.count]);
+        if constexpr (T == 256) {
+            // single-segment problems only (the caller's choice): the 256 x 256
+            // tile has no registers to spare for the segment lookup
+            if (multi)
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL((gemm_group_kernel<CfgL, LAYOUT, BGRAN, CBF16, false>), grid, dim3(CfgL::THREADS), 0,
+                               st, g);
+        } else {
+            if (multi)
+                hipLaunchKernelGGL((gemm_group_kernel<CfgQ, LAYOUT, BGRAN, CBF16, true>), grid, dim3(CfgQ::THREADS), 0,
+                                   st, g);
+            else
+                hipLaunchKernelGGL((gemm_group_kernel<CfgQ, LAYOUT, BGRAN, CBF16, false>), grid, dim3(CfgQ::THREADS),
+                                   0, st, g);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     return hipSuccess;
 }
+
+// 256 x 256 tiles take a group's single-segment NT problems with 128x128 B
+// scales whose M and N are multiples of 256 when they give at least one
+// workgroup per CU;
+// otherwise (and for 1x128 B scales, where they measured slower) the group
+// runs on 128 x 128 tiles.
+constexpr int kLargeGroupMinTiles = kComputeUnits;
 
 template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
@@ -1104,7 +1209,7 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
         } else {
             const GemmArgs a = make_args(p);
             const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-            hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16, false>), grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((gemm_kernel<LAYOUT, BGRAN, CBF16>), grid, dim3(256), 0, st, a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
@@ -1120,7 +1225,30 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
     };
     std::stable_sort(fast.begin(), fast.end(),
                      [&](const GemmArgs &x, const GemmArgs &y) { return blocks(x) > blocks(y); });
-    return launch_group_cfg<CfgQ, LAYOUT, BGRAN, CBF16>(fast, st);
+    std::vector<GemmArgs> large, small;
+    int64_t large_tiles = 0;
+    for (const GemmArgs &x : fast) {
+        if (LAYOUT == 0 && BGRAN == 1 && x.nseg == 1 && x.M % CfgL::TM == 0 && x.N % CfgL::TN == 0) {
+            large.push_back(x);
+            large_tiles += (x.M / CfgL::TM) * (x.N / CfgL::TN);
+        } else {
+            small.push_back(x);
+        }
+    }
+    if (large_tiles < kLargeGroupMinTiles) {
+        small = fast;
+        large.clear();
+    }
+    if constexpr (LAYOUT == 0 && BGRAN == 1) {
+        if (!large.empty()) {
+            const hipError_t e = launch_group_tiles<256, LAYOUT, BGRAN, CBF16>(large, st);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    if (small.empty())
+        return hipSuccess;
+    return launch_group_tiles<128, LAYOUT, BGRAN, CBF16>(small, st);
 }
 
 template <int LAYOUT>
@@ -1134,14 +1262,33 @@ hipError_t launch_group_layout(const GemmProblem *probs, int count, hipStream_t 
                     : launch_group_t<LAYOUT, 0, false>(probs, count, st);
 }
 
+size_t plan_workspace(const GemmProblem &p, int dp)
+{
+    const FastPlan plan = fast_plan(p.M, p.N, p.seg[0].K, dp, p.layout == 0, p.bgran == 1);
+    if (!plan.ok || plan.splits == 1)
+        return 0;
+    return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+}
+
+template <int DP>
+hipError_t launch_aligned(const GemmProblem &p, void *workspace, hipStream_t st)
+{
+    if (p.M == 0 || p.N == 0)
+        return hipSuccess;
+    const GemmArgs a = make_args(p);
+    float *ws = reinterpret_cast<float *>(workspace);
+    switch (p.layout) {
+    case 0: return launch_aligned_layout<0, DP>(p, a, ws, st);
+    case 1: return launch_aligned_layout<1, DP>(p, a, ws, st);
+    default: return launch_aligned_layout<2, DP>(p, a, ws, st);
+    }
+}
+
 } // namespace
 
 size_t gemm_workspace_bytes(const GemmProblem &p)
 {
-    const FastPlan plan = fast_plan(p.M, p.N, p.seg[0].K);
-    if (!plan.ok || plan.splits == 1)
-        return 0;
-    return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+    return plan_workspace(p, DP_F16);
 }
 
 hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st)
@@ -1159,23 +1306,22 @@ hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st)
 
 size_t gemm_mx_workspace_bytes(const GemmProblem &p)
 {
-    const FastPlan plan = fast_plan(p.M, p.N, p.seg[0].K, true);
-    if (!plan.ok || plan.splits == 1)
-        return 0;
-    return (size_t)plan.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+    return plan_workspace(p, DP_MX);
 }
 
 hipError_t launch_gemm_mx(const GemmProblem &p, void *workspace, hipStream_t st)
 {
-    if (p.M == 0 || p.N == 0)
-        return hipSuccess;
-    const GemmArgs a = make_args(p);
-    float *ws = reinterpret_cast<float *>(workspace);
-    switch (p.layout) {
-    case 0: return launch_mx_layout<0>(p, a, ws, st);
-    case 1: return launch_mx_layout<1>(p, a, ws, st);
-    default: return launch_mx_layout<2>(p, a, ws, st);
-    }
+    return launch_aligned<DP_MX>(p, workspace, st);
+}
+
+size_t gemm_native_workspace_bytes(const GemmProblem &p)
+{
+    return plan_workspace(p, DP_FP8);
+}
+
+hipError_t launch_gemm_native(const GemmProblem &p, void *workspace, hipStream_t st)
+{
+    return launch_aligned<DP_FP8>(p, workspace, st);
 }
 
 hipError_t launch_gemm_group(const GemmProblem *probs, int count, hipStream_t st)

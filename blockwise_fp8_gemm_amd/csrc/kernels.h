@@ -79,6 +79,10 @@ hipError_t launch_gemm(const GemmProblem &p, void *workspace, hipStream_t st);
 // Scaled-matrix-core variant: power-of-two scales, M, N, K multiples of 128.
 size_t gemm_mx_workspace_bytes(const GemmProblem &p);
 hipError_t launch_gemm_mx(const GemmProblem &p, void *workspace, hipStream_t st);
+// Native FP8 matrix-core variant: amax/448 scales as in launch_gemm, block
+// partials on the FP8 matrix cores (not FP32-exact), M, N, K multiples of 128.
+size_t gemm_native_workspace_bytes(const GemmProblem &p);
+hipError_t launch_gemm_native(const GemmProblem &p, void *workspace, hipStream_t st);
 // Independent problems sharing layout, B-scale granularity and output dtype;
 // needs no workspace.
 hipError_t launch_gemm_group(const GemmProblem *probs, int count, hipStream_t st);

@@ -327,6 +327,33 @@ puro_status_t puro_fp8_gemm_mx(puro_layout_t layout, int64_t M, int64_t N, int64
                                puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc, void *workspace,
                                size_t ws_bytes, hipStream_t stream);
 
+/*
+ * GEMM with the block partials formed on the native FP8 matrix cores: the
+ * arguments, storage, scales (amax / 448, as written by the quantisers
+ * above) and result definition of puro_fp8_gemm, computed the way the
+ * DeepSeek-V3 design that the Puro-2B report's related-work paragraph cites
+ * computes it -- each 128-wide K block's E4M3 x E4M3 partial on the FP8
+ * matrix cores, promoted into FP32 accumulators as acc += (sA * sB) * partial.
+ * Differences from puro_fp8_gemm:
+ *   - M, N and K must be multiples of 128, and lda and ldb below 2^28 (else
+ *     PURO_ERR_SHAPE; empty products are allowed and do nothing).
+ *   - Precision: the FP8 matrix cores add each run of 8 consecutive products
+ *     in fixed point, dropping bits more than about 13 binary places below the
+ *     run's largest product (measured on gfx950), so a block partial is not
+ *     FP32-exact.  Per element |C - C_exact| <= 2^-9 C_abs + (KB + 4) 2^-23
+ *     C_abs (C_abs: the blockwise product of |A| and |B|); the relative
+ *     Frobenius error is of order 1e-5, against 2e-6 for puro_fp8_gemm.
+ *     Twice the matrix-core peak of puro_fp8_gemm's FP16 datapath.
+ * workspace as for puro_fp8_gemm, sized by puro_fp8_gemm_native_workspace_size
+ * (0 for invalid arguments).
+ */
+size_t puro_fp8_gemm_native_workspace_size(puro_layout_t layout, int64_t M, int64_t N, int64_t K,
+                                           puro_bscale_t bgran);
+puro_status_t puro_fp8_gemm_native(puro_layout_t layout, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                                   int64_t lda, const float *sA, const uint8_t *B, int64_t ldb, const float *sB,
+                                   puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc, void *workspace,
+                                   size_t ws_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *puro_status_string(puro_status_t status);
 

@@ -36,6 +36,7 @@ def test_header_declares_the_calls():
               "puro_fp8_gemm_mx_workspace_size", "puro_status_string",
               "puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2",
               "puro_fp8_swiglu_quant_dual", "puro_fp8_swiglu_quant_dual_pow2",
+              "puro_fp8_gemm_native", "puro_fp8_gemm_native_workspace_size",
               "puro_fp8_version"):
         assert n in names
 
@@ -262,6 +263,40 @@ def test_gemm_mx_validation():
     assert _gmx(M=0, A=NUL, sA=NUL, C=NUL) == OK
     assert pf.puro_fp8_gemm_mx_workspace_size("NT", 200, 256, 256, "1x128") == 0
     assert pf.puro_fp8_gemm_mx_workspace_size("NT", 256, 256, 8192, "1x128") >= 0
+
+
+def _gnat(layout=0, M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, bg=1, C=P, cdt=1, ldc=256,
+          ws=NUL, wsb=0):
+    return pf.lib().puro_fp8_gemm_native(layout, M, N, K, A, lda, sA, B, ldb, sB, bg, C, cdt, ldc, ws, wsb, None)
+
+
+def test_gemm_native_validation():
+    assert _gnat(layout=3) == ENUM
+    assert _gnat(bg=2) == ENUM
+    assert _gnat(cdt=5) == ENUM
+    assert _gnat(M=-1) == SHAPE
+    assert _gnat(ldc=128) == SHAPE
+    assert _gnat(A=NUL) == NULL
+    assert _gnat(sB=NUL) == NULL
+    assert _gnat(C=P_ODD) == ALIGN
+    assert _gnat(lda=264) == ALIGN
+    # extents must be multiples of 128
+    assert _gnat(M=200) == SHAPE
+    assert _gnat(N=136, ldb=256, ldc=256) == SHAPE
+    assert _gnat(K=192) == SHAPE
+    assert _gnat(K=0, A=NUL, sA=NUL, B=NUL, sB=NUL) == SHAPE
+    # leading dimensions of A and B below 2^28
+    assert _gnat(lda=1 << 28) == SHAPE
+    assert _gnat(ldb=1 << 28) == SHAPE
+    # a split-K plan needs its workspace
+    need = pf.puro_fp8_gemm_native_workspace_size("NT", 256, 256, 16384, "1x128")
+    assert need > 0
+    assert _gnat(K=16384, lda=16384, ldb=16384, bg=0) == WORKSPACE
+    assert _gnat(K=16384, lda=16384, ldb=16384, bg=0, ws=P, wsb=need - 1) == WORKSPACE
+    # empty outputs: nothing enqueued
+    assert _gnat(M=0, A=NUL, sA=NUL, C=NUL) == OK
+    assert pf.puro_fp8_gemm_native_workspace_size("NT", 200, 256, 256, "1x128") == 0
+    assert pf.puro_fp8_gemm_native_workspace_size("NN", 256, 256, 256, "128x128") == 0
 
 
 @pytest.mark.parametrize("name", ["puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2"])
