@@ -110,6 +110,8 @@ def lib():
             f = getattr(L, name)
             f.restype = i32
             f.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp, ctypes.c_size_t, vp]
+        L.puro_fp8_gemm_noalloc.restype = i32
+        L.puro_fp8_gemm_noalloc.argtypes = [i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp]
         for name in ("puro_fp8_gemm_mx_workspace_size", "puro_fp8_gemm_native_workspace_size"):
             f = getattr(L, name)
             f.restype = ctypes.c_size_t
@@ -455,6 +457,29 @@ def puro_fp8_gemm(layout, A, sA, B, sB, bgran="128x128", out_dtype=torch.bfloat1
     _check(getattr(lib(), name)(LAYOUTS[layout], M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B), _ptr(sB),
                                 BGRAN[bgran], _ptr(C), PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32,
                                 _ld(C), _ptr(workspace), ws_bytes, _stream(stream)), name)
+    return C
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PURO_NOALLOC_SCRATCH_BYTES
+
+
+@_stream_allocs
+def puro_fp8_gemm_noalloc(layout, A, sA, B, sB, C, bgran="128x128", stream=None):
+    """puro_fp8_gemm into a caller-given C (float32 or bfloat16) with no workspace
+    and no allocation: split-K partials go to the library's fixed device array."""
+    M, N, K = gemm_dims(layout, A, B)
+    if A.dtype != torch.uint8 or B.dtype != torch.uint8:
+        raise TypeError("A and B hold E4M3 codes (torch.uint8)")
+    sa_shape, sb_shape = scale_shapes(layout, bgran, M, N, K)
+    _need_dense(sA, sa_shape, "sA")
+    _need_dense(sB, sb_shape, "sB")
+    if C.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("C is float32 or bfloat16")
+    _need(C, (M, N), C.dtype, "C")
+    _check(lib().puro_fp8_gemm_noalloc(LAYOUTS[layout], M, N, K, _ptr(A), _ld(A), _ptr(sA), _ptr(B), _ld(B),
+                                       _ptr(sB), BGRAN[bgran], _ptr(C),
+                                       PURO_BF16 if C.dtype == torch.bfloat16 else PURO_F32, _ld(C),
+                                       _stream(stream)), "puro_fp8_gemm_noalloc")
     return C
 
 

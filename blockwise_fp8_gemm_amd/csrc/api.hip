@@ -3,6 +3,7 @@
 #include "../../include/puro_fp8.h"
 #include "kernels.h"
 
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -365,6 +366,79 @@ puro_status_t puro_fp8_gemm(puro_layout_t layout, int64_t M, int64_t N, int64_t 
         if (M == 0 || N == 0)
             return PURO_OK;
         return from_hip(puro::launch_gemm(p, workspace, stream));
+    } catch (...) {
+        return PURO_ERR_INTERNAL;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free GEMM: the split-K partial sums go to a fixed device array
+// instead of a caller workspace.  Each GPU the library runs on holds its own
+// copy of `scratch` (PURO_NOALLOC_SCRATCH_BYTES) until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device, with that device current, and
+// only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PURO_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 256;
+static std::mutex g_scratch_mutex;
+static void *g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream).
+static puro_status_t scratch_for_stream(hipStream_t stream, void **out)
+{
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return PURO_ERR_HIP;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess)
+            return PURO_ERR_HIP;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return PURO_ERR_INTERNAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess)
+            return PURO_ERR_HIP;
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess)
+            return PURO_ERR_HIP;
+        if (e != hipSuccess || !ptr)
+            return PURO_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PURO_OK;
+}
+
+puro_status_t puro_fp8_gemm_noalloc(puro_layout_t layout, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                                    int64_t lda, const float *sA, const uint8_t *B, int64_t ldb, const float *sB,
+                                    puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc, hipStream_t stream)
+{
+    try {
+        puro_status_t st = check_gemm(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
+        if (st != PURO_OK)
+            return st;
+        puro::GemmProblem p = make_problem(layout, M, N, K, A, lda, sA, B, ldb, sB, bgran, C, cdt, ldc);
+        // the same plan, kernels and partial-sum layout as puro_fp8_gemm; every
+        // partial is written before it is read, so nothing is cleared
+        const size_t need = puro::gemm_workspace_bytes(p);
+        if (need > (size_t)PURO_NOALLOC_SCRATCH_BYTES)
+            return PURO_ERR_WORKSPACE;
+        if (M == 0 || N == 0)
+            return PURO_OK;
+        void *ws = nullptr;
+        if (need > 0) {
+            st = scratch_for_stream(stream, &ws);
+            if (st != PURO_OK)
+                return st;
+        }
+        return from_hip(puro::launch_gemm(p, ws, stream));
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }

@@ -354,6 +354,27 @@ puro_status_t puro_fp8_gemm_native(puro_layout_t layout, int64_t M, int64_t N, i
                                    puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc, void *workspace,
                                    size_t ws_bytes, hipStream_t stream);
 
+/*
+ * puro_fp8_gemm without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, validation, result and
+ * kernels are those of puro_fp8_gemm; the split-K partial sums go to a fixed
+ * device array of PURO_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).
+ *   - A problem whose plan needs more than PURO_NOALLOC_SCRATCH_BYTES
+ *     (puro_fp8_gemm_workspace_size above it) returns PURO_ERR_WORKSPACE
+ *     before anything is enqueued.
+ *   - All calls on one GPU share that GPU's array: calls that may overlap in
+ *     time on one GPU (other streams, other host threads) race on it and give
+ *     undefined results.  Calls in one stream's order are safe.
+ */
+#define PURO_NOALLOC_SCRATCH_BYTES (64u << 20)
+puro_status_t puro_fp8_gemm_noalloc(puro_layout_t layout, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                                    int64_t lda, const float *sA, const uint8_t *B, int64_t ldb, const float *sB,
+                                    puro_bscale_t bgran, void *C, puro_dtype_t cdt, int64_t ldc,
+                                    hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *puro_status_string(puro_status_t status);
 

@@ -36,7 +36,7 @@ def test_header_declares_the_calls():
               "puro_fp8_gemm_mx_workspace_size", "puro_status_string",
               "puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2",
               "puro_fp8_swiglu_quant_dual", "puro_fp8_swiglu_quant_dual_pow2",
-              "puro_fp8_gemm_native", "puro_fp8_gemm_native_workspace_size",
+              "puro_fp8_gemm_native", "puro_fp8_gemm_native_workspace_size", "puro_fp8_gemm_noalloc",
               "puro_fp8_version"):
         assert n in names
 
@@ -297,6 +297,22 @@ def test_gemm_native_validation():
     assert _gnat(M=0, A=NUL, sA=NUL, C=NUL) == OK
     assert pf.puro_fp8_gemm_native_workspace_size("NT", 200, 256, 256, "1x128") == 0
     assert pf.puro_fp8_gemm_native_workspace_size("NN", 256, 256, 256, "128x128") == 0
+
+
+def test_gemm_noalloc_validation():
+    L = pf.lib()
+
+    def g(layout=0, M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, bg=1, C=P, cdt=1, ldc=256):
+        return L.puro_fp8_gemm_noalloc(layout, M, N, K, A, lda, sA, B, ldb, sB, bg, C, cdt, ldc, None)
+    assert g(layout=3) == ENUM
+    assert g(M=-1) == SHAPE
+    assert g(A=NUL) == NULL
+    assert g(C=P_ODD) == ALIGN
+    # a plan needing more than the fixed array is rejected before any HIP call
+    assert pf.puro_fp8_gemm_workspace_size("NT", 384, 5504, 16384, "1x128") > pf.NOALLOC_SCRATCH_BYTES
+    assert g(M=384, N=5504, K=16384, lda=16384, ldb=16384, bg=0, ldc=5504) == WORKSPACE
+    # empty output: nothing to do
+    assert g(M=0, A=NUL, sA=NUL, C=NUL) == OK
 
 
 @pytest.mark.parametrize("name", ["puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2"])
