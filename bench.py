@@ -20,8 +20,13 @@ Inputs are seeded synthetic tensors already resident in HBM: activations
 BF16 N(0,1), gradients BF16 N(0,1e-3), FP32 master weights N(0,0.02), fresh
 per layer.  Output: one JSON line (see the end of main()).  Besides the step,
 the gated activation fused into the dual quantiser (the down projection's
-input formed from the gate/up product) is timed on its own and reported under
-"side_kernels"; it is not part of the step or of its FLOP rate.
+input formed from the gate/up product), other GEMM forms and the whole step on
+the native-FP8 and scaled (MX) matrix-core variants are timed on their own and
+reported under "side_kernels"; none is part of the step or of its FLOP rate.
+After the timing, the oracle leg (skipped with --no-cpu-baseline) checks the
+timed step's last layer -- every code and scale byte and sampled entries of
+its 15 GEMM outputs -- against the CPU oracle ("parity"), times the oracle on a
+sample of the workload ("cpu_baseline") and per configuration ("configs").
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -61,8 +66,14 @@ class Plan:
                 raise RuntimeError("C-ABI call failed with status %d" % st)
 
 
-def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
-    """Allocate the stack's inputs (seeded, on the GPU) and outputs; return (plan, keepalive).
+def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr, datapath="exact", resident=None):
+    """Allocate the stack's inputs (seeded, on the GPU; or reuse `resident`, an earlier plan's) and
+    outputs; return (plan, keepalive, buffers).
+
+    datapath: "exact" -- the recipe on the FP32-exact GEMMs (the benchmarked step);
+              "native" -- the same quantisers, GEMMs on the native FP8 matrix cores
+                          (puro_fp8_gemm_native, one call per product);
+              "mx" -- power-of-two quantisers and the scaled matrix cores (puro_fp8_gemm_mx).
 
     The projections that read one input (q/k/v; gate/up) keep their weights' codes in adjacent
     rows of one buffer and their outputs and output gradients in adjacent columns, as a fused
@@ -112,18 +123,40 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
     dx = {x: torch.empty((T, c), dtype=bf16, device=dev) for x, c in synth.LAYER_INPUTS}
     dw = {g: torch.empty((n, k), dtype=f32, device=dev) for g, n, k, _ in synth.LAYER_GEMMS}
     keep += [qx, sx, qxt, sxt, qdy, sdy, qdyt, sdyt, qw, sw, qwt, swt, y, dx, dw]
+    bufs = {"qx": qx, "sx": sx, "qxt": qxt, "sxt": sxt, "qdy": qdy, "sdy": sdy, "qdyt": qdyt, "sdyt": sdyt,
+            "qw": qw, "sw": sw, "qwt": qwt, "swt": swt, "y": y, "dx": dx, "dw": dw, "rows": {}, "inputs": []}
 
     BF16, F32 = pf.PURO_BF16, pf.PURO_F32
     NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
     S1, S128 = pf.BGRAN["1x128"], pf.BGRAN["128x128"]
 
+    single = {"native": (L.puro_fp8_gemm_native, L.puro_fp8_gemm_native_workspace_size),
+              "mx": (L.puro_fp8_gemm_mx, L.puro_fp8_gemm_mx_workspace_size)}.get(datapath)
+    ws_need = []       # (plan index, workspace bytes) of single calls, patched once the buffer exists
+
     def grouped(layout, bgran, cdt, descs, name, flops):
-        arr = (pf.GemmDesc * len(descs))(*descs)
-        keep.append(arr)
-        plan.add(L.puro_fp8_gemm_grouped, (layout, bgran, cdt, arr, len(descs), stream_ptr), "gemm", name, flops)
+        if single is None:
+            arr = (pf.GemmDesc * len(descs))(*descs)
+            keep.append(arr)
+            plan.add(L.puro_fp8_gemm_grouped, (layout, bgran, cdt, arr, len(descs), stream_ptr), "gemm", name,
+                     flops)
+            return
+        # one call per problem (these variants have no grouped launcher); one shared workspace
+        for d in descs:
+            sg = d.seg[0]
+            K = sg.K
+            need = single[1](layout, d.M, d.N, K, bgran)
+            ws_need.append((len(plan.calls), need))
+            plan.add(single[0], [layout, d.M, d.N, K, vp(sg.A), sg.lda, vp(sg.sA), vp(sg.B), sg.ldb, vp(sg.sB),
+                                 bgran, vp(d.C), cdt, d.ldc, None, 0, stream_ptr], "gemm", name,
+                     2.0 * d.M * d.N * K)
+
+    quant_dual_fn = L.puro_fp8_quant_dual_pow2 if datapath == "mx" else L.puro_fp8_quant_dual
+    quant_weight_fn = (L.puro_fp8_quant_weight_grouped_pow2 if datapath == "mx"
+                       else L.puro_fp8_quant_weight_grouped)
 
     def dual(x, c, q, s, qt, st):
-        plan.add(L.puro_fp8_quant_dual, (P(x), BF16, T, c, c, P(q), c, P(s), 1, P(qt), T, P(st), stream_ptr),
+        plan.add(quant_dual_fn, (P(x), BF16, T, c, c, P(q), c, P(s), 1, P(qt), T, P(st), stream_ptr),
                  "quant_dual", "quant_dual", 0, T * c * (2 + 2 + 8 / 128))
 
     def fwd(G):
@@ -149,24 +182,28 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
 
     group_of = {g: G for G, (_, _, _, members, _) in grp.items() for g in members}
     for layer in range(layers):
-        xs = {x: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
-              for i, (x, c) in enumerate(synth.LAYER_INPUTS)}
-        # FP32 master weights, those of one group in adjacent rows of one tensor
-        wts = {G: torch.empty((n, k), dtype=f32, device=dev) for G, (n, k, _, _, _) in grp.items()}
-        for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS):
-            G = group_of[g]
-            r0 = grp[G][4][g]
-            wts[G][r0:r0 + n] = synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
-        dys = {G: synth.device_normal((T, grp[G][0]), 1e-3, synth.seed_of(4, layer, 30 + j), "bf16", dev)
-               for j, (G, _, _) in enumerate(synth.PROJ_GROUPS)}
+        if resident is not None:
+            xs, wts, dys = resident[layer]
+        else:
+            xs = {x: synth.device_normal((T, c), 1.0, synth.seed_of(4, layer, i), "bf16", dev)
+                  for i, (x, c) in enumerate(synth.LAYER_INPUTS)}
+            # FP32 master weights, those of one group in adjacent rows of one tensor
+            wts = {G: torch.empty((n, k), dtype=f32, device=dev) for G, (n, k, _, _, _) in grp.items()}
+            for j, (g, n, k, _) in enumerate(synth.LAYER_GEMMS):
+                G = group_of[g]
+                r0 = grp[G][4][g]
+                wts[G][r0:r0 + n] = synth.device_normal((n, k), 0.02, synth.seed_of(4, layer, 10 + j), "f32", dev)
+            dys = {G: synth.device_normal((T, grp[G][0]), 1e-3, synth.seed_of(4, layer, 30 + j), "bf16", dev)
+                   for j, (G, _, _) in enumerate(synth.PROJ_GROUPS)}
         keep += [xs, wts, dys]
+        bufs["inputs"].append((xs, wts, dys))
         # the layer's weights quantised in one grouped launch (128x128 tiles; the tiles of a
         # group's weights are those of each weight), each group's codes also transposed
         descs = [pf.QuantWeightDesc(P(wts[G]), n, k, k, P(qw[G]), k, P(sw[G]), P(qwt[G]), n, P(swt[G]))
                  for G, (n, k, _, _, _) in grp.items()]
         wd = (pf.QuantWeightDesc * len(descs))(*descs)
         keep.append(wd)
-        plan.add(L.puro_fp8_quant_weight_grouped, (F32, wd, len(descs), stream_ptr),
+        plan.add(quant_weight_fn, (F32, wd, len(descs), stream_ptr),
                  "quant_weight", "quant_weight", 0,
                  sum(n * k * (4 + 2) + 2 * nb(n) * nb(k) * 4 for _, n, k, _ in synth.LAYER_GEMMS))
         # forward: each input quantised once both ways (the 128-token copy is kept for the
@@ -184,7 +221,144 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr):
             grouped(NT, S128, BF16, [dgrad(G)], "gemm_dgrad_NT_128x128_bf16", fl(G))
         grouped(NT, S1, F32, [wgrad(g, group_of[g]) for g, _, _, _ in synth.LAYER_GEMMS],
                 "gemm_wgrad_NT_1x128_f32", sum(2.0 * T * n * k for _, n, k, _ in synth.LAYER_GEMMS))
-    return plan, keep
+    bufs["rows"] = {g: grp[group_of[g]][4][g] for g, _, _, _ in synth.LAYER_GEMMS}
+    if ws_need:
+        ws = torch.empty(max(max(n for _, n in ws_need), 256), dtype=u8, device=dev)
+        keep.append(ws)
+        for idx, need in ws_need:
+            fn, a, kind, name, fl, nbyt = plan.calls[idx]
+            a[14], a[15] = P(ws), need
+            plan.calls[idx] = (fn, tuple(a), kind, name, fl, nbyt)
+    return plan, keep, bufs
+
+
+def oracle_check_of_timed_layer(torch, bufs, samples=3000):
+    """Oracle leg, part one: the timed step's last layer, checked after the timing.
+
+    The step reuses its work buffers from layer to layer, so after the timed steps they hold
+    the last layer's codes, scales and products.  That layer's inputs (drawn on the GPU) are
+    copied to the host; every code and scale byte of its quantisers is compared with the
+    oracle's, and `samples` entries of each of its 15 GEMM outputs (4 forward products, 4
+    data gradients, 7 weight gradients) with the oracle's FP64 products of the oracle's
+    codes, within the per-element bound (KB + 4) 2^-23 C_abs (plus one BF16 rounding for
+    BF16 outputs).  Returns the summary reported as "parity" in the JSON line."""
+    import numpy as np
+    import oracle
+    import synth
+    T = synth.TOKENS
+    layer = len(bufs["inputs"]) - 1
+    xs, wts, dys = bufs["inputs"][layer]
+
+    def h(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    def same(got, ref):
+        got, ref = np.asarray(got), np.asarray(ref)
+        if got.dtype == np.float32:
+            got, ref = got.view(np.uint32), ref.astype(np.float32).view(np.uint32)
+        return int(got.size), int(np.count_nonzero(got != ref))
+
+    nbytes = mism = 0
+
+    def cmp(got, ref):
+        nonlocal nbytes, mism
+        n_, m_ = same(h(got), ref)
+        nbytes += n_
+        mism += m_
+
+    ref = {}
+    for src, _ in synth.LAYER_INPUTS:
+        x = h(xs[src])
+        qa, sa = oracle.quant_act(x)
+        qt, st = oracle.quant_transpose(x, True)
+        cmp(bufs["qx"][src], qa); cmp(bufs["sx"][src], sa)
+        cmp(bufs["qxt"][src], qt); cmp(bufs["sxt"][src], st)
+        ref["x", src] = (qa, sa, qt, st)
+    for G, _, _ in synth.PROJ_GROUPS:
+        dy = h(dys[G])
+        qa, sa = oracle.quant_act(dy)
+        qt, st = oracle.quant_transpose(dy, True)
+        cmp(bufs["qdy"][G], qa); cmp(bufs["sdy"][G], sa)
+        cmp(bufs["qdyt"][G], qt); cmp(bufs["sdyt"][G], st)
+        qw, sw = oracle.quant_weight(h(wts[G]))
+        cmp(bufs["qw"][G], qw); cmp(bufs["sw"][G], sw)
+        cmp(bufs["qwt"][G], qw.T); cmp(bufs["swt"][G], sw.T)
+        ref["dy", G] = (qa, sa, qt, st)
+        ref["w", G] = (qw, sw)
+
+    rng = np.random.default_rng(20261203)
+    worst, checked, failed = 0.0, 0, 0
+    worst_rel = {False: 0.0, True: 0.0}   # relative Frobenius error of the samples, FP32 / BF16 outputs
+
+    def entries(layout, A, sA, B, sB, bgran, K, got_t, bf16_out):
+        nonlocal worst, checked, failed
+        M, N = got_t.shape
+        ms, ns = rng.integers(0, M, samples), rng.integers(0, N, samples)
+        ms[:4], ns[:4] = [0, 0, M - 1, M - 1], [0, N - 1, 0, N - 1]
+        A, sA, B, sB = (np.ascontiguousarray(v) for v in (A, sA, B, sB))
+        r = oracle.gemm_entries(layout, A, sA, B, sB, bgran, ms, ns)
+        c_abs = oracle.gemm_entries(layout, A & 0x7F, np.abs(sA), B & 0x7F, np.abs(sB), bgran, ms, ns)
+        E = (K // 128 + 4) * 2.0 ** -23 * c_abs
+        g = h(got_t)[ms, ns]
+        if bf16_out:
+            g = (g.astype(np.uint32) << 16).view(np.float32)
+            E = E + 2.0 ** -8 * (np.abs(r) + E)
+        err = np.abs(g.astype(np.float64) - r)
+        ratio = err / np.where(E > 0, E, np.inf)
+        worst = max(worst, float(np.max(np.where(E > 0, ratio, np.where(err > 0, np.inf, 0.0)))))
+        worst_rel[bf16_out] = max(worst_rel[bf16_out], float(np.linalg.norm(err) / max(np.linalg.norm(r), 1e-300)))
+        checked += samples
+        failed += int(np.count_nonzero(err > E))
+
+    shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
+    for G, members, src in synth.PROJ_GROUPS:
+        qa, sa, _, _ = ref["x", src]
+        qw, sw = ref["w", G]
+        K_in = qa.shape[1]
+        entries("NT", qa, sa, qw, sw, "128x128", K_in, bufs["y"][G], True)                 # forward
+        qd, sd, _, _ = ref["dy", G]
+        entries("NT", qd, sd, qw.T, sw.T, "128x128", qd.shape[1], bufs["dx"][src], True)    # data gradient
+        for g in members:                                                                   # weight gradients
+            n, k, _ = shape[g]
+            r0 = bufs["rows"][g]
+            _, _, qdt, sdt = ref["dy", G]
+            _, _, qxt, sxt = ref["x", src]
+            entries("NT", qdt[r0:r0 + n], sdt[r0:r0 + n], qxt, sxt, "1x128", T, bufs["dw"][g], False)
+    ok = mism == 0 and failed == 0
+    return {"layer": layer, "pass": bool(ok), "quantiser_bytes_compared": nbytes, "quantiser_mismatches": mism,
+            "gemm_outputs": 15, "gemm_entries_checked": checked, "gemm_entries_over_bound": failed,
+            "max_err_over_bound": round(worst, 4),
+            "max_rel_frobenius_fp32_outputs": float("%.3g" % worst_rel[False]),
+            "max_rel_frobenius_bf16_outputs": float("%.3g" % worst_rel[True])}
+
+
+def step_side_figure(torch, plan, stream, steps, step_flops):
+    """Time a variant of the step (2 warm-up steps, then `steps` steps, event-timed), then once
+    more with an event between launches for its GEMM share."""
+    for _ in range(2):
+        plan.run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        plan.run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan.calls) + 1)]
+    evs[0].record(stream)
+    for j, (fn, args, _, _, _, _) in enumerate(plan.calls):
+        if fn(*args):
+            raise RuntimeError("C-ABI call failed")
+        evs[j + 1].record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = sum(evs[j].elapsed_time(evs[j + 1]) for j, c in enumerate(plan.calls) if c[2] == "gemm")
+    return {"ms_per_step": round(ms, 3), "TFLOP/s": round(step_flops / (ms * 1e-3) / 1e12, 1),
+            "gemm_ms": round(gemm_ms, 3), "gemm_TFLOP/s": round(step_flops / (gemm_ms * 1e-3) / 1e12, 1),
+            "launches": len(plan.calls)}
 
 
 def swiglu_setup(pf, torch, dev, tokens, sp):
@@ -481,6 +655,77 @@ def cpu_baseline(rows):
                       % (rows, rows, rows, flops / 1e9, t_total)}
 
 
+def oracle_configs(rows=32):
+    """Oracle leg, per configuration of the workload table: the oracle's quantisers (GB/s over
+    their algorithmic bytes) and blockwise GEMMs (GFLOP/s, FP64) timed on a stated sample of
+    that configuration's inputs, with the thread count used.  Config 1 runs whole; the others
+    quantise and multiply `rows` rows of each operand that carries the tokens (and the whole
+    weights), and for their weight gradients `rows` x 256 outputs over all tokens."""
+    import numpy as np
+    import oracle
+    import synth
+    T = synth.TOKENS
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def entry(q_bytes, q_s, flops, g_s, sample):
+        return {"quant_GB/s": round(q_bytes / q_s / 1e9, 3), "gemm_GFLOP/s": round(flops / g_s / 1e9, 3),
+                "threads": oracle.num_threads(), "sample": sample}
+
+    # config 1, whole
+    X = synth.normal((256, 512), 1.0, synth.seed_of(1, 0, 0))
+    W = synth.normal((256, 512), 1.0, synth.seed_of(1, 0, 1))
+    r = {}
+    q_s = timed(lambda: r.update(a=oracle.quant_act(X), w=oracle.quant_weight(W)))
+    g_s = timed(lambda: oracle.gemm("NT", *r["a"], *r["w"], "128x128"))
+    out["1_single_fwd"] = entry(2 * 256 * 512 * (4 + 1) + 256 * 4 * 4 + 8 * 4, q_s, 2.0 * 256 * 256 * 512, g_s,
+                                "whole configuration")
+    # configs 2 and 3: the fused four-GEMM layer
+    q2 = g2 = q3 = g3 = 0.0
+    qb2 = fl2 = qb3 = fl3 = 0.0
+    for i, (g, n, k) in enumerate(synth.FUSED_GEMMS):
+        X = synth.normal((rows, k), 1.0, synth.seed_of(2, 0, i), "bf16")
+        W = synth.normal((n, k), 0.02, synth.seed_of(2, 0, 10 + i))
+        dY = synth.normal((128, n), 1e-3, synth.seed_of(3, 0, 20 + i), "bf16")
+        Xt = synth.normal((T, 256), 1.0, synth.seed_of(3, 0, 30 + i), "bf16")
+        dYt = synth.normal((T, rows), 1e-3, synth.seed_of(3, 0, 40 + i), "bf16")
+        q2 += timed(lambda: r.update(a=oracle.quant_act(X), w=oracle.quant_weight(W)))
+        qb2 += rows * k * (2 + 1 + 4 / 128) + n * k * 5
+        g2 += timed(lambda: oracle.gemm("NT", *r["a"], *r["w"], "128x128"))
+        fl2 += 2.0 * rows * n * k
+        q3 += timed(lambda: r.update(d=oracle.quant_act(dY), dt=oracle.quant_transpose(dY, True),
+                                     xt=oracle.quant_transpose(Xt, True), yt=oracle.quant_transpose(dYt, True)))
+        qb3 += 128 * n * (2 + 2 + 8 / 128) + (T * 256 + T * rows) * (2 + 1 + 4 / 128)
+        g3 += timed(lambda: oracle.gemm("NN", r["d"][0][:rows], r["d"][1][:rows], *r["w"], "128x128"))
+        g3 += timed(lambda: oracle.gemm("NT", *r["yt"], *r["xt"], "1x128"))
+        fl3 += 2.0 * rows * k * n + 2.0 * rows * 256 * T
+    out["2_layer_fwd"] = entry(qb2, q2, fl2, g2, "%d of 8,192 token rows per GEMM, whole weights" % rows)
+    out["3_layer_bwd"] = entry(qb3, q3, fl3, g3, "dgrad: %d token rows (a 128-token block quantised); wgrad: "
+                                                 "%d x 256 outputs over all 8,192 tokens" % (rows, rows))
+    # config 5
+    T5, N5, K5 = 16384, 2048, 6144
+    X, _ = synth.outlier_activations(128, K5, synth.seed_of(5, 0, 0))
+    dY = synth.lognormal_gradients(128, N5, synth.seed_of(5, 0, 1))
+    W = synth.normal((N5, K5), 0.02, synth.seed_of(5, 0, 2))
+    Xt, _ = synth.outlier_activations(T5, 128, synth.seed_of(5, 0, 3))
+    dYt = synth.lognormal_gradients(T5, 128, synth.seed_of(5, 0, 4))
+    q5 = timed(lambda: r.update(a=oracle.quant_act(X), w=oracle.quant_weight(W), d=oracle.quant_act(dY),
+                                xt=oracle.quant_transpose(Xt, True), yt=oracle.quant_transpose(dYt, True)))
+    qb5 = 128 * (K5 + N5) * (2 + 1 + 4 / 128) + N5 * K5 * 5 + 2 * T5 * 128 * (2 + 1 + 4 / 128)
+    g5 = timed(lambda: oracle.gemm("NT", r["a"][0][:rows], r["a"][1][:rows], *r["w"], "128x128"))
+    g5 += timed(lambda: oracle.gemm("NN", r["d"][0][:rows], r["d"][1][:rows], *r["w"], "128x128"))
+    g5 += timed(lambda: oracle.gemm("NT", r["yt"][0][:rows], r["yt"][1][:rows], *r["xt"], "1x128"))
+    fl5 = 2.0 * rows * N5 * K5 * 2 + 2.0 * rows * 128 * T5
+    out["5_outlier_stress"] = entry(qb5, q5, fl5, g5, "%d token rows (fwd, dgrad) and %d output rows x 128 "
+                                                      "channels over all 16,384 tokens (wgrad); 128-row blocks "
+                                                      "quantised" % (rows, rows))
+    return out
+
+
 # Measured HBM traffic per launch of each GEMM kind (rocprofv3 FETCH_SIZE and
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size).  It
 # holds only for the kernel source it was measured on, identified by hash.
@@ -513,8 +758,9 @@ def measured_traffic(name):
 
 
 def traffic_probe():
-    """One layer of the step, three times, the fused activation + dual quantiser three times, then
-    a plain 1 GiB copy three times (the calibration for the memory counters); run under
+    """One layer of the step three times, then the same layer on the native-FP8 and on the
+    scaled (MX) datapaths three times each, the fused activation + dual quantiser three times,
+    then a plain 1 GiB copy three times (the calibration for the memory counters); run under
     rocprofv3 --pmc."""
     import torch
     import blockwise_fp8_gemm_amd as pf
@@ -522,9 +768,16 @@ def traffic_probe():
     torch.cuda.set_device(dev)
     sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     import synth
-    plan, keep = build_stack_plan(pf, torch, dev, 1, synth.TOKENS, sp)
+    plan, keep, bufs = build_stack_plan(pf, torch, dev, 1, synth.TOKENS, sp)
     for _ in range(3):
         plan.run()
+    for dp in ("native", "mx"):
+        plan_d, keep_d, _ = build_stack_plan(pf, torch, dev, 1, synth.TOKENS, sp, datapath=dp,
+                                             resident=bufs["inputs"])
+        for _ in range(3):
+            plan_d.run()
+        torch.cuda.synchronize()
+        del plan_d, keep_d
     fn, args, _, keep_sw = swiglu_setup(pf, torch, dev, synth.TOKENS, sp)
     for _ in range(3):
         if fn(*args):
@@ -534,8 +787,8 @@ def traffic_probe():
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print("traffic probe done: 1 layer x 3, the fused activation x 3, then copy of %d bytes x 3"
-          % src.numel(), flush=True)
+    print("traffic probe done: 1 layer x 3 on each of the exact, native and mx datapaths, the fused "
+          "activation x 3, then copy of %d bytes x 3" % src.numel(), flush=True)
 
 
 def main():
@@ -570,7 +823,7 @@ def main():
     tokens = synth.TOKENS
 
     t0 = time.time()
-    plan, keep = build_stack_plan(pf, torch, dev, args.layers, tokens, sp)
+    plan, keep, bufs = build_stack_plan(pf, torch, dev, args.layers, tokens, sp)
     torch.cuda.synchronize()
     log("inputs resident: %d layers, %.1f GB allocated, %d launches per step (%.1fs)"
         % (args.layers, torch.cuda.memory_allocated() / 1e9, len(plan.calls), time.time() - t0))
@@ -621,10 +874,42 @@ def main():
             k, v[0] / args.steps, v[3] // args.steps, v[0] / v[3] * 1e3,
             ("%.0f TFLOP/s" % (v[1] / v[0] / 1e9)) if v[1] else ("%.0f GB/s" % (v[2] / v[0] / 1e6))))
 
-    side = {"swiglu_quant_dual": swiglu_side(pf, torch, dev, tokens, sp, args.steps)}
-    side.update(gemm_side(pf, torch, dev, tokens, sp, args.steps))
+    # Oracle leg, part one (skipped with --no-cpu-baseline): the timed run's own outputs
+    parity = None
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        log("checking the timed step's last layer against the oracle ...")
+        t1 = time.time()
+        parity = oracle_check_of_timed_layer(torch, bufs)
+        log("  parity of layer %d: %s (%d quantiser bytes, %d mismatches; %d GEMM entries, %d over the bound, "
+            "max err/bound %.3f) in %.1fs" % (parity["layer"], "pass" if parity["pass"] else "FAIL",
+                                               parity["quantiser_bytes_compared"], parity["quantiser_mismatches"],
+                                               parity["gemm_entries_checked"], parity["gemm_entries_over_bound"],
+                                               parity["max_err_over_bound"], time.time() - t1))
+    inputs = bufs["inputs"]
+    del bufs
     del plan, keep
     torch.cuda.empty_cache()
+
+    # The same step (same resident inputs) on the two FP8-matrix-core variants, as side
+    # figures: the native FP8 partials with the recipe's scales, and the power-of-two
+    # quantisers with the scaled (MX) matrix cores.  Neither is the benchmarked step.
+    side_steps = {}
+    for dp in ("native", "mx"):
+        plan_d, keep_d, _ = build_stack_plan(pf, torch, dev, args.layers, tokens, sp, datapath=dp,
+                                             resident=inputs)
+        side_steps[dp] = step_side_figure(torch, plan_d, stream, max(3, args.steps // 2), step_flops)
+        log("  %s step (outside the benchmarked step): %.3f ms/step, %.0f TFLOP/s (GEMMs %.3f ms, %.0f TFLOP/s)"
+            % (dp, side_steps[dp]["ms_per_step"], side_steps[dp]["TFLOP/s"], side_steps[dp]["gemm_ms"],
+               side_steps[dp]["gemm_TFLOP/s"]))
+        del plan_d, keep_d
+        torch.cuda.empty_cache()
+    del inputs
+    torch.cuda.empty_cache()
+
+    side = {"swiglu_quant_dual": swiglu_side(pf, torch, dev, tokens, sp, args.steps)}
+    side.update(gemm_side(pf, torch, dev, tokens, sp, args.steps))
+    side["steps"] = side_steps
     configs = measure_configs(pf, torch, dev, sp) if not args.no_configs else None
 
     dom_name, dom = max(per_name.items(), key=lambda kv: kv[1][0])
@@ -670,10 +955,20 @@ def main():
         "roofline": roofline,
         "side_kernels": side,
         "configs": configs,
+        "parity": parity,
     }
+    if configs:
+        for name, res in configs.items():
+            res["pct_fp8_peak"] = round(100.0 * res["hot_tflops"] / FP8_PEAK_TFLOPS, 2)
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        if configs:
+            log("timing the oracle per configuration on samples ...")
+            for name, res in oracle_configs().items():
+                configs[name]["oracle"] = res
+                log("  config %-18s oracle: quantisers %.3f GB/s, GEMM %.3f GFLOP/s (%d threads; %s)"
+                    % (name, res["quant_GB/s"], res["gemm_GFLOP/s"], res["threads"], res["sample"]))
     print(json.dumps(out), flush=True)
 
 

@@ -970,23 +970,23 @@ constexpr int kComputeUnits = 256;
 // tiles run two per CU (`step2`, `fixed2` each pair) and `step1`, `fixed1`
 // when one is left alone.
 struct TileCost {
-    double step2, fixed2, step1, fixed1;
+    double step2, fixed2, step1, fixed1, launch;   // launch: once per launch
 };
 
 TileCost tile_cost(int cfg, int dp)
 {
     if (cfg == CFG_Q) {
         if (dp == DP_F16)
-            return {1.96, 4.1, 1.4, 3.0};
+            return {1.96, 4.1, 1.4, 3.0, 0.0};
         if (dp == DP_MX)
-            return {1.07, 5.6, 0.8, 4.0};
-        return {1.24, 2.2, 0.9, 2.0};
+            return {1.07, 5.6, 0.8, 4.0, 0.0};
+        return {1.24, 2.2, 0.9, 2.0, 0.0};
     }
     if (dp == DP_F16)
-        return {3.6, 13.4, 3.6, 13.4};
+        return {3.6, 8.0, 3.6, 8.0, 6.0};
     if (dp == DP_MX)
-        return {2.13, 6.1, 2.13, 6.1};
-    return {2.24, 6.1, 2.24, 6.1};
+        return {2.13, 6.1, 2.13, 6.1, 0.0};
+    return {2.24, 6.1, 2.24, 6.1, 0.0};
 }
 
 // Picks the candidate with the least estimated time.  Workgroups are spread
@@ -1017,7 +1017,7 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K, int dp, bool nt, bool bgran1
             const int64_t per_cu = (tiles * sp + kComputeUnits - 1) / kComputeUnits;
             double us = cfg == CFG_Q ? (double)(per_cu / 2) * (steps * c.step2 + c.fixed2) +
                                            (double)(per_cu % 2) * (steps * c.step1 + c.fixed1)
-                                     : (double)per_cu * (steps * c.step1 + c.fixed1);
+                                     : (double)per_cu * (steps * c.step1 + c.fixed1) + c.launch;
             if (sp > 1)
                 us += (double)(sp + 1) * (double)M * (double)N * 4.0 / 4e6 + 5.0;
             if (us < best_us) {
@@ -1183,12 +1183,24 @@ hipError_t launch_group_tiles(const std::vector<GemmArgs> &ps, hipStream_t st)
     return hipSuccess;
 }
 
-// 256 x 256 tiles take a group's single-segment NT problems with 128x128 B
-// scales whose M and N are multiples of 256 when they give at least one
-// workgroup per CU;
-// otherwise (and for 1x128 B scales, where they measured slower) the group
-// runs on 128 x 128 tiles.
-constexpr int kLargeGroupMinTiles = kComputeUnits;
+// Estimated time of a group's problems on one tile configuration of the
+// FP32-exact datapath (the per-tile costs of fast_plan, work spread evenly
+// over the CUs).
+double group_estimate(const std::vector<GemmArgs> &ps, int cfg)
+{
+    const TileCost c = tile_cost(cfg, DP_F16);
+    const int T = cfg == CFG_Q ? CfgQ::TM : CfgL::TM;
+    double work = 0.0;
+    for (const GemmArgs &x : ps) {
+        int64_t blocks = 0;
+        for (int j = 0; j < x.nseg; j++)
+            blocks += x.seg[j].KB;
+        const double tiles = (double)((x.M / T) * (x.N / T));
+        work += cfg == CFG_Q ? tiles * ((double)blocks * c.step2 + c.fixed2) / 2.0
+                             : tiles * ((double)blocks * c.step1 + c.fixed1);
+    }
+    return work / kComputeUnits + c.launch;
+}
 
 template <int LAYOUT, int BGRAN, bool CBF16>
 hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
@@ -1226,16 +1238,16 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
     std::stable_sort(fast.begin(), fast.end(),
                      [&](const GemmArgs &x, const GemmArgs &y) { return blocks(x) > blocks(y); });
     std::vector<GemmArgs> large, small;
-    int64_t large_tiles = 0;
     for (const GemmArgs &x : fast) {
         if (LAYOUT == 0 && BGRAN == 1 && x.nseg == 1 && x.M % CfgL::TM == 0 && x.N % CfgL::TN == 0) {
             large.push_back(x);
-            large_tiles += (x.M / CfgL::TM) * (x.N / CfgL::TN);
         } else {
             small.push_back(x);
         }
     }
-    if (large_tiles < kLargeGroupMinTiles) {
+    // the 256 x 256 tiles (measured faster for NT with 128x128 B scales, slower
+    // for 1x128) take the eligible problems when the estimate favours them
+    if (large.empty() || group_estimate(large, CFG_L) >= group_estimate(large, CFG_Q)) {
         small = fast;
         large.clear();
     }

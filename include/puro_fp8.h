@@ -76,6 +76,10 @@ typedef enum { PURO_SCALE_1x128 = 0, PURO_SCALE_128x128 = 1 } puro_bscale_t;
 
 /*
  * Activation / gradient quantiser (1x128 along each row).
+ * Passage: Puro-2B-Base model card (friendli.ai), training-setup paragraph
+ * under the Phase 1 / Phase 2 table -- the main linear-layer GEMMs run in
+ * blockwise E4M3, so each GEMM's activation and gradient operands are
+ * quantised to E4M3 with per-block scales before the product.
  *   x   [rows][cols], FP32 or BF16 (xdt), row stride ldx
  *   q   [rows][cols] E4M3 codes, row stride ldq
  *   s   [rows][ceil(cols/128)] FP32, dense
@@ -89,6 +93,9 @@ puro_status_t puro_fp8_quant_act(const void *x, puro_dtype_t xdt, int64_t rows, 
 
 /*
  * Weight quantiser (128x128 tiles).
+ * Passage: the same setup paragraph -- master weights stay in BF16 or FP32,
+ * and the main GEMMs that read them run in blockwise E4M3, so each GEMM takes
+ * an E4M3 copy of its FP32 (or BF16) master weight.
  *   w   [rows][cols], FP32 or BF16 (wdt) master weight, row stride ldw
  *   q   [rows][cols] E4M3 codes, row stride ldq
  *   s   [ceil(rows/128)][ceil(cols/128)] FP32, dense
@@ -132,6 +139,10 @@ puro_status_t puro_fp8_quant_weight_grouped(puro_dtype_t wdt, const puro_quant_w
                                             int count, hipStream_t stream);
 
 /*
+ * Passage: the same setup paragraph (the blockwise E4M3 GEMMs include the
+ * backward ones) and the technical report's related-work paragraph on FP8
+ * mixed precision (part 7/7): the weight-gradient product contracts over the
+ * tokens, so its operands dY and X are blocked along the tokens.
  * Token-dimension quantiser for the weight-gradient GEMM: blocks are 128
  * consecutive tokens of one column of x [tokens][cols] (FP32 or BF16, stride ldx).
  *   transpose_out = 1: q [cols][tokens] (stride ldq), s [cols][ceil(tokens/128)]
@@ -193,7 +204,10 @@ size_t puro_fp8_gemm_workspace_size(puro_layout_t layout, int64_t M, int64_t N, 
                                     puro_bscale_t bgran);
 
 /*
- * Blockwise-scaled FP8 GEMM:
+ * Blockwise-scaled FP8 GEMM.
+ * Passage: the setup paragraph (main linear-layer GEMMs in blockwise E4M3,
+ * FP32 kept where needed) and the related-work paragraph's DeepSeek-V3 design
+ * (FP8 block products promoted into FP32 accumulators):
  *   C[m][n] = sum_kb sA(m,kb) * sB(n,kb) * sum_{k in block kb} a(m,k) b(k,n)
  * with a, b the E4M3 values of A and B, kb over the ceil(K/128) blocks of K.
  * Storage (KB = ceil(K/128), NB = ceil(N/128)); scales are dense and indexed

@@ -99,12 +99,17 @@ def test_layer_gemm_full_size(dev, g, n_out, k_in):
     _check_sampled("NT", "1x128", (rqdt, rsdt, rqxt, rsxt), dWg, T, 3, torch.float32)
 
 
-def test_outlier_stress_full_size(dev):
-    """Down-projection shape at 16,384 tokens: 1% of channels x100, lognormal gradients,
-    all-zero 128-blocks; forward, data gradient, weight gradient (FP32 outputs)."""
+@pytest.mark.parametrize("random_sign", [False, True], ids=["positive_dY", "random_sign_dY"])
+def test_outlier_stress_full_size(dev, random_sign):
+    """Down-projection shape at 16,384 tokens: 1% of channels x100, lognormal gradients
+    (the literal positive ones, and the random-sign variant the outlier-stress row lists as a
+    parity-only extra), all-zero 128-blocks; forward, data gradient, weight gradient (FP32
+    outputs)."""
     T, K_in, N_out = 16384, 6144, 2048
     X, _ = synth.outlier_activations(T, K_in, synth.seed_of(5, 0, 0))
-    dY = synth.lognormal_gradients(T, N_out, synth.seed_of(5, 0, 1))
+    dY = synth.lognormal_gradients(T, N_out, synth.seed_of(5, 0, 1), random_sign=random_sign)
+    if random_sign:
+        assert (synth.bf16_bits_to_f32(dY) < 0).mean() > 0.45
     W = synth.normal((N_out, K_in), 0.02, synth.seed_of(5, 0, 2))
     dX_, dW_, ddY = to_dev(X), to_dev(W), to_dev(dY)
     rqx, rsx = oracle.quant_act(X)
