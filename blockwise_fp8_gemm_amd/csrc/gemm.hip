@@ -671,9 +671,16 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             // all JT tiles so that no MFMA waits on the one just issued.  Larger
             // wave tiles (not INTERLEAVE) have no registers to spare for that:
             // each row block is read and widened whole, and each tile's four
-            // MFMAs run back to back with one partial live.
+            // MFMAs run back to back.  There a tile's promotion waits until
+            // the next tile's MFMAs are issued (two partials live), so that
+            // its FMAs do not wait for the matrix core to drain the chain
+            // they read; one scheduling barrier per row block keeps the
+            // compiler from hoisting the next row block's work into this one
+            // (which costs registers the tile does not have).
             constexpr bool INTERLEAVE = IT * JT <= 16;
             v8i araw = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
+            v4f prev_P = {0.0f, 0.0f, 0.0f, 0.0f};   // the last tile's partial, not yet promoted
+            float prev_s[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // and its scales
 #pragma unroll
             for (int i = 0; i < IT; i++) {
                 const float4 sa4 = *reinterpret_cast<const float4 *>(&LSC[wrow + i * 16 + 4 * (lane >> 4)]);
@@ -713,10 +720,24 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
 #pragma unroll
                         for (int q = 1; q < 4; q++)
                             P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[q], bh[j].c[q], P, 0, 0, 0);
+                        if (i > 0 || j > 0) {
+                            // the tile before this one (compile-time indices)
+                            const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : JT - 1;
+#pragma unroll
+                            for (int r = 0; r < 4; r++)
+                                acc[pi][pj][r] = fmaf(prev_s[r], prev_P[r], acc[pi][pj][r]);
+                        }
+                        prev_P = P;
 #pragma unroll
                         for (int r = 0; r < 4; r++)
-                            acc[i][j][r] = fmaf(scale(j, r), P[r], acc[i][j][r]);
+                            prev_s[r] = scale(j, r);
                     }
+                    if (i == IT - 1) {
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            acc[IT - 1][JT - 1][r] = fmaf(prev_s[r], prev_P[r], acc[IT - 1][JT - 1][r]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
