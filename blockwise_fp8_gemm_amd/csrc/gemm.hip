@@ -670,13 +670,10 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
             // as the last sub-step of this one is widened; each sub-step runs over
             // all JT tiles so that no MFMA waits on the one just issued.  Larger
             // wave tiles (not INTERLEAVE) have no registers to spare for that:
-            // each row block is read and widened whole, and each tile's four
-            // MFMAs run back to back.  There a tile's promotion waits until
-            // the next tile's MFMAs are issued (two partials live), so that
-            // its FMAs do not wait for the matrix core to drain the chain
-            // they read; one scheduling barrier per row block keeps the
-            // compiler from hoisting the next row block's work into this one
-            // (which costs registers the tile does not have).
+            // there each tile's four MFMAs run back to back, and a tile's
+            // promotion waits until the next tile's MFMAs are issued (two
+            // partials live), so that its FMAs do not wait for the matrix core
+            // to drain the chain they read.
             constexpr bool INTERLEAVE = IT * JT <= 16;
             v8i araw = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
             v4f prev_P = {0.0f, 0.0f, 0.0f, 0.0f};   // the last tile's partial, not yet promoted
@@ -710,34 +707,53 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                         for (int r = 0; r < 4; r++)
                             acc[i][j][r] = fmaf(scale(j, r), P[j][r], acc[i][j][r]);
                 } else {
-                    if (i > 0)
-                        araw = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
-                    const V8H4 ah = widen32(araw);
+                    // Row block i, in issue order: tile 0's four MFMAs, each after
+                    // the widening of its K step of A; then tiles 1..JT-1, the
+                    // MFMAs of each tile back to back.  After every MFMA comes one
+                    // promotion FMA of the tile before (its chain has drained by
+                    // then) and a scheduling fence, so that the compiler keeps the
+                    // MFMAs spread among the vector instructions instead of
+                    // bunching them.  The next row block's A fragment is read
+                    // after tile 0, once this block's scale read has been waited
+                    // for, so that the wait for the scales does not also wait for
+                    // it; it lands during tiles 1..JT-1.
+                    v8h ahq[4];
+                    const float sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+                    float rsc[4];   // sA sB of this lane's rows (128x128 B scales) or sA
 #pragma unroll
                     for (int j = 0; j < JT; j++) {
-                        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                        v4f P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[0], bh[j].c[0], zero, 0, 0, 0);
+                        v4f P;
 #pragma unroll
-                        for (int q = 1; q < 4; q++)
-                            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.c[q], bh[j].c[q], P, 0, 0, 0);
-                        if (i > 0 || j > 0) {
-                            // the tile before this one (compile-time indices)
-                            const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : JT - 1;
-#pragma unroll
-                            for (int r = 0; r < 4; r++)
-                                acc[pi][pj][r] = fmaf(prev_s[r], prev_P[r], acc[pi][pj][r]);
+                        for (int q = 0; q < 4; q++) {
+                            if (j == 0)
+                                ahq[q] = widen8(araw, q);
+                            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahq[q], bh[j].c[q], q ? P : zero, 0, 0, 0);
+                            if (i > 0 || j > 0) {
+                                // the tile before this one (compile-time indices)
+                                const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : JT - 1;
+                                acc[pi][pj][q] = fmaf(prev_s[q], prev_P[q], acc[pi][pj][q]);
+                            }
+                            if (j == 1 && q == 0 && i + 1 < IT)
+                                araw = A_KMAJ ? fast_frag_k(ta, wrow + (i + 1) * 16, lane)
+                                              : fast_frag_mn<TM>(ta, wrow + (i + 1) * 16, lane);
+                            __builtin_amdgcn_sched_barrier(0);
                         }
                         prev_P = P;
+                        if (j == 0) {
+#pragma unroll
+                            for (int r = 0; r < 4; r++)
+                                rsc[r] = BGRAN ? sav[r] * sbv[0] : sav[r];
+                        }
 #pragma unroll
                         for (int r = 0; r < 4; r++)
-                            prev_s[r] = scale(j, r);
+                            prev_s[r] = BGRAN ? rsc[r] : rsc[r] * sbv[j];
                     }
                     if (i == IT - 1) {
 #pragma unroll
                         for (int r = 0; r < 4; r++)
                             acc[IT - 1][JT - 1][r] = fmaf(prev_s[r], prev_P[r], acc[IT - 1][JT - 1][r]);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
@@ -994,7 +1010,7 @@ struct TileCost {
     double step2, fixed2, step1, fixed1, launch;   // launch: once per launch
 };
 
-TileCost tile_cost(int cfg, int dp)
+TileCost tile_cost(int cfg, int dp, bool bgran128)
 {
     if (cfg == CFG_Q) {
         if (dp == DP_F16)
@@ -1003,8 +1019,8 @@ TileCost tile_cost(int cfg, int dp)
             return {1.07, 5.6, 0.8, 4.0, 0.0};
         return {1.24, 2.2, 0.9, 2.0, 0.0};
     }
-    if (dp == DP_F16)
-        return {3.6, 8.0, 3.6, 8.0, 6.0};
+    if (dp == DP_F16)   // 1x128 B scales: one more product per promoted element
+        return bgran128 ? TileCost{3.3, 8.0, 3.3, 8.0, 6.0} : TileCost{3.67, 8.0, 3.67, 8.0, 6.0};
     if (dp == DP_MX)
         return {2.13, 6.1, 2.13, 6.1, 0.0};
     return {2.24, 6.1, 2.24, 6.1, 0.0};
@@ -1014,8 +1030,7 @@ TileCost tile_cost(int cfg, int dp)
 // evenly over the CUs, so the busiest CU sets the time.  Splitting K adds the
 // partial sums, (splits + 1) M N 4 bytes moved at about 4 TB/s, and the
 // reduction launch.  On the FP32-exact datapath the 256 x 256 tile is
-// considered for NT products with 128x128 B scales only, the one case where
-// it measured faster.
+// considered for NT products only (its K-major fragments).
 FastPlan fast_plan(int64_t M, int64_t N, int64_t K, int dp, bool nt, bool bgran128)
 {
     FastPlan best = {false, CFG_Q, 1};
@@ -1024,12 +1039,12 @@ FastPlan fast_plan(int64_t M, int64_t N, int64_t K, int dp, bool nt, bool bgran1
     const int64_t KB = K / 128;
     double best_us = 1e300;
     for (int cfg : {(int)CFG_L, (int)CFG_Q}) {
-        if (cfg == CFG_L && dp == DP_F16 && !(nt && bgran128))
+        if (cfg == CFG_L && dp == DP_F16 && !nt)
             continue;
         const int T = cfg == CFG_Q ? CfgQ::TM : CfgL::TM;
         if (M % T || N % T)
             continue;
-        const TileCost c = tile_cost(cfg, dp);
+        const TileCost c = tile_cost(cfg, dp, bgran128);
         const int64_t tiles = (M / T) * (N / T);
         for (int sp = 1; sp <= 8; sp *= 2) {
             if (sp > 1 && KB / sp < 4)
@@ -1086,8 +1101,8 @@ template <int LAYOUT, int BGRAN, bool CBF16, int DP>
 hipError_t launch_planned(const GemmArgs &a, const FastPlan &plan, float *ws, hipStream_t st)
 {
     if (plan.cfg == CFG_L) {
-        // the FP32-exact datapath plans 256 x 256 tiles for NT with 128x128 B scales only
-        if constexpr (DP != DP_F16 || (LAYOUT == 0 && BGRAN == 1))
+        // the FP32-exact datapath plans 256 x 256 tiles for NT only
+        if constexpr (DP != DP_F16 || LAYOUT == 0)
             return launch_fast_cfg<CfgL, LAYOUT, BGRAN, CBF16, DP>(a, plan.splits, ws, st);
         return hipErrorInvalidValue;
     }
@@ -1207,9 +1222,9 @@ hipError_t launch_group_tiles(const std::vector<GemmArgs> &ps, hipStream_t st)
 // Estimated time of a group's problems on one tile configuration of the
 // FP32-exact datapath (the per-tile costs of fast_plan, work spread evenly
 // over the CUs).
-double group_estimate(const std::vector<GemmArgs> &ps, int cfg)
+double group_estimate(const std::vector<GemmArgs> &ps, int cfg, bool bgran128)
 {
-    const TileCost c = tile_cost(cfg, DP_F16);
+    const TileCost c = tile_cost(cfg, DP_F16, bgran128);
     const int T = cfg == CFG_Q ? CfgQ::TM : CfgL::TM;
     double work = 0.0;
     for (const GemmArgs &x : ps) {
@@ -1260,19 +1275,18 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
                      [&](const GemmArgs &x, const GemmArgs &y) { return blocks(x) > blocks(y); });
     std::vector<GemmArgs> large, small;
     for (const GemmArgs &x : fast) {
-        if (LAYOUT == 0 && BGRAN == 1 && x.nseg == 1 && x.M % CfgL::TM == 0 && x.N % CfgL::TN == 0) {
+        if (LAYOUT == 0 && x.nseg == 1 && x.M % CfgL::TM == 0 && x.N % CfgL::TN == 0) {
             large.push_back(x);
         } else {
             small.push_back(x);
         }
     }
-    // the 256 x 256 tiles (measured faster for NT with 128x128 B scales, slower
-    // for 1x128) take the eligible problems when the estimate favours them
-    if (large.empty() || group_estimate(large, CFG_L) >= group_estimate(large, CFG_Q)) {
+    // the 256 x 256 tiles take the eligible problems when the estimate favours them
+    if (large.empty() || group_estimate(large, CFG_L, BGRAN == 1) >= group_estimate(large, CFG_Q, BGRAN == 1)) {
         small = fast;
         large.clear();
     }
-    if constexpr (LAYOUT == 0 && BGRAN == 1) {
+    if constexpr (LAYOUT == 0) {
         if (!large.empty()) {
             const hipError_t e = launch_group_tiles<256, LAYOUT, BGRAN, CBF16>(large, st);
             if (e != hipSuccess)
