@@ -609,10 +609,29 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                 sbe[j] = e8m0(BGRAN ? LSC[TM + (wcol >> 7)] : LSC[TM + wcol + j * 16 + (lane & 15)]);
                 bf[j] = B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane) : fast_frag_mn<TN>(tb, wcol + j * 16, lane);
             }
+            // On 256 x 256 tiles each row block's A fragment and scale are read
+            // one row block ahead (before this block's MFMAs are issued, a fence
+            // keeping the order), so that the MFMAs never wait for the LDS read
+            // just before them.  The 128 x 128 tiles, two workgroups per CU,
+            // measured faster with the compiler's own order.
+            constexpr bool PREFETCH = NW > 4;
+            v8i af_next = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
+            float sa_next = LSC[wrow + (lane & 15)];
 #pragma unroll
             for (int i = 0; i < IT; i++) {
-                const v8i af = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
-                const int sae = e8m0(LSC[wrow + i * 16 + (lane & 15)]);
+                if (!PREFETCH && i > 0) {
+                    af_next = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
+                    sa_next = LSC[wrow + i * 16 + (lane & 15)];
+                }
+                const v8i af = af_next;
+                const int sae = e8m0(sa_next);
+                if (PREFETCH && i + 1 < IT) {
+                    af_next = A_KMAJ ? fast_frag_k(ta, wrow + (i + 1) * 16, lane)
+                                     : fast_frag_mn<TM>(ta, wrow + (i + 1) * 16, lane);
+                    sa_next = LSC[wrow + (i + 1) * 16 + (lane & 15)];
+                }
+                if (PREFETCH)
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < JT; j++) {
                     v4f c = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
@@ -621,6 +640,8 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                     for (int r = 0; r < 4; r++)
                         acc[i][j][r] = c[r];
                 }
+                if (PREFETCH)
+                    __builtin_amdgcn_sched_barrier(0);
             }
         } else if constexpr (DP == DP_FP8) {
             // Native FP8 matrix cores: one v_mfma_f32_16x16x128_f8f6f4 per 16x16
@@ -634,20 +655,50 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                 sbv[j] = BGRAN ? LSC[TM + (wcol >> 7)] : LSC[TM + wcol + j * 16 + (lane & 15)];
                 bf[j] = B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane) : fast_frag_mn<TN>(tb, wcol + j * 16, lane);
             }
+            // As on the MX path, each row block's A fragment and scales are read
+            // one row block ahead (except on 256 x 256 tiles with an N-contiguous
+            // B, whose transposing reads leave no registers for it); and, as on
+            // the FP16 path, a tile's promotion runs after the next tile's MFMA
+            // is issued, so that its FMAs do not wait for the matrix core.
+            constexpr bool PREFETCH = B_KMAJ || NW <= 4;
+            v8i af_next = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
+            float4 sa_next = *reinterpret_cast<const float4 *>(&LSC[wrow + 4 * (lane >> 4)]);
+            v4f prev_P = {0.0f, 0.0f, 0.0f, 0.0f};
+            float prev_s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < IT; i++) {
-                const v8i af = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
-                const float4 sa4 = *reinterpret_cast<const float4 *>(&LSC[wrow + i * 16 + 4 * (lane >> 4)]);
-                const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+                if (!PREFETCH && i > 0) {
+                    af_next = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
+                    sa_next = *reinterpret_cast<const float4 *>(&LSC[wrow + i * 16 + 4 * (lane >> 4)]);
+                }
+                const v8i af = af_next;
+                const float sa[4] = {sa_next.x, sa_next.y, sa_next.z, sa_next.w};
+                if (PREFETCH && i + 1 < IT) {
+                    af_next = A_KMAJ ? fast_frag_k(ta, wrow + (i + 1) * 16, lane)
+                                     : fast_frag_mn<TM>(ta, wrow + (i + 1) * 16, lane);
+                    sa_next = *reinterpret_cast<const float4 *>(&LSC[wrow + (i + 1) * 16 + 4 * (lane >> 4)]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < JT; j++) {
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                     const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
+                    if (i > 0 || j > 0) {
+                        const int pi = j > 0 ? i : i - 1, pj = j > 0 ? j - 1 : JT - 1;
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            acc[pi][pj][r] = fmaf(prev_s[r], prev_P[r], acc[pi][pj][r]);
+                    }
+                    prev_P = P;
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        acc[i][j][r] = fmaf(sa[r] * sbv[j], P[r], acc[i][j][r]);
+                        prev_s[r] = sa[r] * sbv[j];
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                acc[IT - 1][JT - 1][r] = fmaf(prev_s[r], prev_P[r], acc[IT - 1][JT - 1][r]);
         } else {
 
             // B's scales: with 128x128 weight tiles the wave's JT * 16 columns lie in
