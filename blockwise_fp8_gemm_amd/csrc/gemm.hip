@@ -294,18 +294,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
 //   MN-major tile [128 k][W B]: segment s of row k at s ^ mnswz<W>(k)
 // ===========================================================================
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v2i lds_v2i_t;
 
-__device__ __forceinline__ void load_lds16(const void *g, uint8_t *lds_wave_base)
+// Direct copies from global memory to LDS (global_load_lds_*): lane l's bytes
+// land at the LDS address in M0 plus size * l.  They are written as inline
+// assembly, not through the compiler's builtin.  While a builtin copy is in
+// flight the compiler treats every LDS read as completing out of order and
+// waits for each with lgkmcnt(0), so a fragment read a row block ahead was
+// waited for as soon as the next one was needed.  The hardware counts these
+// copies in the vector-memory counter, which the K loop waits on explicitly
+// (s_waitcnt before its barrier, and before the epilogue reuses a stage).
+// Should the LDS counter also count them, a wait for it only becomes stricter.
+// Each statement sets M0 itself; no other instruction of these kernels reads
+// M0 (gfx9 and later LDS instructions do not).  The memory clobber keeps the
+// copies in program order with every other memory access.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_wave_base, 16, 0, 0);
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// M0 is a reserved register, and clang says so about the clobber below; the
+// clobber is kept so that the compiler knows M0 changed.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from base + off (base wave-uniform, off a 32-bit per-lane
+// byte offset).
+__device__ __forceinline__ void load_lds16(const uint8_t *base, uint32_t off, uint8_t *lds_wave_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
+}
+
+// 4 bytes per lane from the lane's own address g.
 __device__ __forceinline__ void load_lds4(const void *g, void *lds_wave_base)
 {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_wave_base, 4, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Swizzle of K-major stages: 16-byte segment s of row r sits at s ^ kswz(r).
 // A fragment read (lane i: row base + i % 16, 16 bytes) then touches 16
@@ -332,8 +358,9 @@ __device__ __forceinline__ int mnswz(int k)
 
 // The copies below address global memory as a wave-uniform base (scalar
 // registers: the wave number is uniform) plus a 32-bit per-lane offset of at
-// most 7 rows (the fast path needs leading dimensions below 2^28), so that
-// the per-block address arithmetic runs on the scalar unit.
+// most 7 rows (the fast path needs leading dimensions below 2^28), the
+// instruction's scalar-base form, so that the per-block address arithmetic
+// runs on the scalar unit.
 
 // Rows [row0, row0+ROWS) x bytes [k0, k0+128) of a K-contiguous operand, NW waves.
 template <int ROWS, int NW>
@@ -347,10 +374,7 @@ __device__ __forceinline__ void fast_stage_k(uint8_t *t, const uint8_t *g, int64
         const int seg = (lane & 7) ^ (((lane >> 3) & 7) ^ (c & 1));   // kswz(8c + lane / 8)
         const uint8_t *base = g + (row0 + 8 * c) * ld + k0;
         const uint32_t off = (uint32_t)(lane >> 3) * (uint32_t)ld + (uint32_t)(seg * 16);
-        // opaque scalar base: the compiler cannot re-associate it with the lane
-        // offset into a 64-bit per-lane address, and emits the base + offset form
-        asm volatile("" : "+s"(base));
-        load_lds16(base + off, t + c * 1024);
+        load_lds16(base, off, t + c * 1024);
     }
 }
 
@@ -367,8 +391,7 @@ __device__ __forceinline__ void fast_stage_mn(uint8_t *t, const uint8_t *g, int6
         const int seg = (lane % SEGS) ^ mnswz<W>(c * RPC + lane / SEGS);
         const uint8_t *base = g + (k0 + RPC * c) * ld + mn0;
         const uint32_t off = (uint32_t)(lane / SEGS) * (uint32_t)ld + (uint32_t)(seg * 16);
-        asm volatile("" : "+s"(base));   // as in fast_stage_k
-        load_lds16(base + off, t + c * 1024);
+        load_lds16(base, off, t + c * 1024);
     }
 }
 
@@ -609,29 +632,21 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                 sbe[j] = e8m0(BGRAN ? LSC[TM + (wcol >> 7)] : LSC[TM + wcol + j * 16 + (lane & 15)]);
                 bf[j] = B_KMAJ ? fast_frag_k(tb, wcol + j * 16, lane) : fast_frag_mn<TN>(tb, wcol + j * 16, lane);
             }
-            // On 256 x 256 tiles each row block's A fragment and scale are read
-            // one row block ahead (before this block's MFMAs are issued, a fence
-            // keeping the order), so that the MFMAs never wait for the LDS read
-            // just before them.  The 128 x 128 tiles, two workgroups per CU,
-            // measured faster with the compiler's own order.
-            constexpr bool PREFETCH = NW > 4;
+            // Each row block's A fragment and scale are read one row block ahead
+            // (before this block's MFMAs are issued, a fence keeping the order),
+            // so that the MFMAs never wait for the LDS read just before them.
             v8i af_next = A_KMAJ ? fast_frag_k(ta, wrow, lane) : fast_frag_mn<TM>(ta, wrow, lane);
             float sa_next = LSC[wrow + (lane & 15)];
 #pragma unroll
             for (int i = 0; i < IT; i++) {
-                if (!PREFETCH && i > 0) {
-                    af_next = A_KMAJ ? fast_frag_k(ta, wrow + i * 16, lane) : fast_frag_mn<TM>(ta, wrow + i * 16, lane);
-                    sa_next = LSC[wrow + i * 16 + (lane & 15)];
-                }
                 const v8i af = af_next;
                 const int sae = e8m0(sa_next);
-                if (PREFETCH && i + 1 < IT) {
+                if (i + 1 < IT) {
                     af_next = A_KMAJ ? fast_frag_k(ta, wrow + (i + 1) * 16, lane)
                                      : fast_frag_mn<TM>(ta, wrow + (i + 1) * 16, lane);
                     sa_next = LSC[wrow + (i + 1) * 16 + (lane & 15)];
                 }
-                if (PREFETCH)
-                    __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < JT; j++) {
                     v4f c = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
@@ -640,8 +655,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                     for (int r = 0; r < 4; r++)
                         acc[i][j][r] = c[r];
                 }
-                if (PREFETCH)
-                    __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else if constexpr (DP == DP_FP8) {
             // Native FP8 matrix cores: one v_mfma_f32_16x16x128_f8f6f4 per 16x16
