@@ -993,13 +993,20 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_fast_kernel(GemmArgs arg
                                                              kb_lo, kb_hi, split, ws);
 }
 
-// Several independent problems in one launch: problem i owns workgroups
-// [first[i], first[i+1]), one per output tile, walked as in gemm_fast_kernel.
+// Several independent problems in one launch: problem i owns tiles
+// [first[i], first[i+1]) of the launch, walked as in gemm_fast_kernel.
+// Workgroups reach the 8 XCDs round-robin.  With xcd_whole each XCD takes a
+// contiguous eighth of the launch's tiles: one or two whole problems, or a
+// contiguous part of one, so that the tiles resident together on an XCD share
+// operand panels in its L2 (the host asks for it when every problem has the
+// same number of K blocks, which keeps the eighths equal in work).  Otherwise
+// each XCD takes a contiguous eighth of every problem's tiles.
 constexpr int kGroupMax = 8;
 struct GroupArgs {
     GemmArgs p[kGroupMax];
     int first[kGroupMax + 1];
     int count;
+    int xcd_whole;
 };
 
 template <class Cfg, int LAYOUT, int BGRAN, bool CBF16, bool MULTI, int DP = DP_F16>
@@ -1008,7 +1015,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_group_kernel(GroupArgs a
     (void)args;   // read through the argument segment pointer below
     typedef __attribute__((address_space(4))) const GroupArgs *KernargGroup;
     const KernargGroup gp = (KernargGroup)__builtin_amdgcn_kernarg_segment_ptr();
-    const int b = blockIdx.x;
+    const bool whole = gp->xcd_whole != 0;
+    const int b = whole ? xcd_contiguous(blockIdx.x, gp->first[gp->count]) : blockIdx.x;
     int i = 0;
     while (i + 1 < gp->count && b >= gp->first[i + 1])
         i++;
@@ -1018,7 +1026,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 2) void gemm_group_kernel(GroupArgs a
     const GemmArgs p = load_args(&gp->p[i]);
     const int first = gp->first[i];
     const int tiles_m = (int)(p.M / Cfg::TM), tiles_n = (int)(p.N / Cfg::TN);
-    const int t = xcd_contiguous(b - first, tiles_m * tiles_n);
+    const int t = whole ? b - first : xcd_contiguous(b - first, tiles_m * tiles_n);
     int tm, tn;
     tile_coords(t, tiles_m, tiles_n, tm, tn);
     int64_t blocks = 0;
@@ -1252,10 +1260,21 @@ hipError_t launch_group_tiles(const std::vector<GemmArgs> &ps, hipStream_t st)
         GroupArgs g;
         g.count = (int)std::min(ps.size() - lo, (size_t)kGroupMax);
         g.first[0] = 0;
+        bool same_k = true;
         for (int i = 0; i < g.count; i++) {
             g.p[i] = ps[lo + i];
             g.first[i + 1] = g.first[i] + (int)((g.p[i].M / T) * (g.p[i].N / T));
+            int64_t kb = 0, kb0 = 0;
+            for (int j = 0; j < g.p[i].nseg; j++)
+                kb += g.p[i].seg[j].KB;
+            for (int j = 0; j < g.p[0].nseg; j++)
+                kb0 += g.p[0].seg[j].KB;
+            same_k = same_k && kb == kb0;
         }
+#ifndef PURO_XCD_WHOLE
+#define PURO_XCD_WHOLE 1
+#endif
+        g.xcd_whole = PURO_XCD_WHOLE && g.count > 1 && same_k && g.first[g.count] % 8 == 0;
         // launches whose problems all have one K segment take the kernel
         // without the segment lookup
         bool multi = false;
