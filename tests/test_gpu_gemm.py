@@ -246,6 +246,30 @@ def test_grouped_more_problems_than_one_launch(dev):
         _check_product("NT", "128x128", hostops, devops, torch.float32, C=C)
 
 
+# Equally deep problems whose tile count is a multiple of 8: the launch hands
+# each XCD a contiguous eighth of all its tiles, so eighths start and end inside
+# problems (128x128 tiles: 6+6+5+4+3 = 24; 256x256-eligible extents: 16 tiles).
+EQUAL_DEPTH = {
+    "tiles128": ([(256, 384), (384, 256), (128, 640), (512, 128), (128, 384)], 640),
+    "tiles256": ([(512, 512), (256, 768), (768, 256), (512, 512), (512, 256)], 1024),
+}
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("group", sorted(EQUAL_DEPTH))
+def test_grouped_equal_depth_xcd_eighths(dev, group, out):
+    shapes, K = EQUAL_DEPTH[group]
+    for bgran in ("1x128", "128x128"):
+        ops = []
+        for i, (M, N) in enumerate(shapes):
+            X = synth.normal((M, K), 1.0, 3600 + i)
+            W = synth.normal((N, K), 0.02, 3700 + i)
+            ops.append(_quantise_both("NT", bgran, X, W))
+        Cs = pf.puro_fp8_gemm_grouped("NT", [dv for _, dv in ops], bgran=bgran, out_dtype=out)
+        for (hostops, devops), C in zip(ops, Cs):
+            _check_product("NT", bgran, hostops, devops, out, C=C)
+
+
 def test_grouped_layer_projections_reduced_tokens(dev):
     # the q, k, v projections of one input and the gate/up pair, 512 tokens:
     # grouped forward products equal the single calls' to the parity bound
