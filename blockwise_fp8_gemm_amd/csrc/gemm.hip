@@ -296,6 +296,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p)
 
 typedef __attribute__((address_space(3))) v2i lds_v2i_t;
 
+// GEMM outputs are stored non-temporally (`nt`): the kernel never reads them
+// back, and the hint keeps hundreds of MB of dirty output lines from sitting
+// in the caches, where their write-back slowed the quantiser launched next by
+// about 10% (measured in the benchmarked step: dual quantiser 8.6 -> 7.7 ms per
+// step, weight quantiser 1.94 -> 1.74 ms, the GEMMs unchanged).
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_out_nt(uint4 *p, uint4 v)
+{
+    const v4u_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<v4u_t *>(p));
+}
+__device__ __forceinline__ void store_out_nt(float4 *p, float4 v)
+{
+    const v4f w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<v4f *>(p));
+}
+__device__ __forceinline__ void store_out_nt(uint2 *p, uint2 v)
+{
+    const v2u_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<v2u_t *>(p));
+}
+
 // Direct copies from global memory to LDS (global_load_lds_*): lane l's bytes
 // land at the LDS address in M0 plus size * l.  They are written as inline
 // assembly, not through the compiler's builtin.  While a builtin copy is in
@@ -941,7 +964,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                 o.y = to_bf16x2(a.z, a.w);
                 o.z = to_bf16x2(b.x, b.y);
                 o.w = to_bf16x2(b.z, b.w);
-                *dst = o;
+                store_out_nt(dst, o);
             } else {
                 float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(gC) + m * ldc + n);
                 float4 o = v0;
@@ -949,7 +972,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs &p, int64_t m0, int64_t
                     const float4 c = *dst;
                     o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
                 }
-                *dst = o;
+                store_out_nt(dst, o);
             }
         }
     }
@@ -1070,9 +1093,9 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(const float *__restrict
     if (CBF16) {
         const uint32_t lo = to_bf16x2(sum.x, sum.y);
         const uint32_t hi = to_bf16x2(sum.z, sum.w);
-        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(C) + m * ldc + n) = make_uint2(lo, hi);
+        store_out_nt(reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(C) + m * ldc + n), make_uint2(lo, hi));
     } else {
-        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(C) + m * ldc + n) = sum;
+        store_out_nt(reinterpret_cast<float4 *>(reinterpret_cast<float *>(C) + m * ldc + n), sum);
     }
 }
 
