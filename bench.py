@@ -72,8 +72,10 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr, datapath="exact
 
     datapath: "exact" -- the recipe on the FP32-exact GEMMs (the benchmarked step);
               "native" -- the same quantisers, GEMMs on the native FP8 matrix cores
-                          (puro_fp8_gemm_native, one call per product);
-              "mx" -- power-of-two quantisers and the scaled matrix cores (puro_fp8_gemm_mx).
+                          (puro_fp8_gemm_grouped_native);
+              "mx" -- power-of-two quantisers and the scaled matrix cores (puro_fp8_gemm_grouped_mx).
+    Every datapath runs the same launches: per layer one grouped weight quantisation, 8 dual
+    quantisations and 9 grouped GEMM calls.
 
     The projections that read one input (q/k/v; gate/up) keep their weights' codes in adjacent
     rows of one buffer and their outputs and output gradients in adjacent columns, as a fused
@@ -130,26 +132,13 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr, datapath="exact
     NT, NN = pf.LAYOUTS["NT"], pf.LAYOUTS["NN"]
     S1, S128 = pf.BGRAN["1x128"], pf.BGRAN["128x128"]
 
-    single = {"native": (L.puro_fp8_gemm_native, L.puro_fp8_gemm_native_workspace_size),
-              "mx": (L.puro_fp8_gemm_mx, L.puro_fp8_gemm_mx_workspace_size)}.get(datapath)
-    ws_need = []       # (plan index, workspace bytes) of single calls, patched once the buffer exists
+    grouped_fn = {"exact": L.puro_fp8_gemm_grouped, "native": L.puro_fp8_gemm_grouped_native,
+                  "mx": L.puro_fp8_gemm_grouped_mx}[datapath]
 
     def grouped(layout, bgran, cdt, descs, name, flops):
-        if single is None:
-            arr = (pf.GemmDesc * len(descs))(*descs)
-            keep.append(arr)
-            plan.add(L.puro_fp8_gemm_grouped, (layout, bgran, cdt, arr, len(descs), stream_ptr), "gemm", name,
-                     flops)
-            return
-        # one call per problem (these variants have no grouped launcher); one shared workspace
-        for d in descs:
-            sg = d.seg[0]
-            K = sg.K
-            need = single[1](layout, d.M, d.N, K, bgran)
-            ws_need.append((len(plan.calls), need))
-            plan.add(single[0], [layout, d.M, d.N, K, vp(sg.A), sg.lda, vp(sg.sA), vp(sg.B), sg.ldb, vp(sg.sB),
-                                 bgran, vp(d.C), cdt, d.ldc, None, 0, stream_ptr], "gemm", name,
-                     2.0 * d.M * d.N * K)
+        arr = (pf.GemmDesc * len(descs))(*descs)
+        keep.append(arr)
+        plan.add(grouped_fn, (layout, bgran, cdt, arr, len(descs), stream_ptr), "gemm", name, flops)
 
     quant_dual_fn = L.puro_fp8_quant_dual_pow2 if datapath == "mx" else L.puro_fp8_quant_dual
     quant_weight_fn = (L.puro_fp8_quant_weight_grouped_pow2 if datapath == "mx"
@@ -222,13 +211,6 @@ def build_stack_plan(pf, torch, dev, layers, tokens, stream_ptr, datapath="exact
         grouped(NT, S1, F32, [wgrad(g, group_of[g]) for g, _, _, _ in synth.LAYER_GEMMS],
                 "gemm_wgrad_NT_1x128_f32", sum(2.0 * T * n * k for _, n, k, _ in synth.LAYER_GEMMS))
     bufs["rows"] = {g: grp[group_of[g]][4][g] for g, _, _, _ in synth.LAYER_GEMMS}
-    if ws_need:
-        ws = torch.empty(max(max(n for _, n in ws_need), 256), dtype=u8, device=dev)
-        keep.append(ws)
-        for idx, need in ws_need:
-            fn, a, kind, name, fl, nbyt = plan.calls[idx]
-            a[14], a[15] = P(ws), need
-            plan.calls[idx] = (fn, tuple(a), kind, name, fl, nbyt)
     return plan, keep, bufs
 
 

@@ -16,6 +16,7 @@ Names mirror the C entry points:
     puro_fp8_gemm_workspace_size(layout, M, N, K, bgran)
     puro_fp8_gemm(..., mx=True)           -> puro_fp8_gemm_mx (power-of-two scales, scaled matrix cores)
     puro_fp8_gemm(..., native=True)       -> puro_fp8_gemm_native (partials on the FP8 matrix cores)
+    puro_fp8_gemm_grouped(..., mx=True / native=True) -> the grouped forms of those two
     puro_status_string(status)
 Tensors are 2-D, row-major (stride(1) == 1), with a row stride that is a
 multiple of 16 elements and 16-byte aligned storage.
@@ -120,8 +121,10 @@ def lib():
             f = getattr(L, name)
             f.restype = i32
             f.argtypes = [i32, ctypes.POINTER(QuantWeightDesc), i32, vp]
-        L.puro_fp8_gemm_grouped.restype = i32
-        L.puro_fp8_gemm_grouped.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, vp]
+        for name in ("puro_fp8_gemm_grouped", "puro_fp8_gemm_grouped_mx", "puro_fp8_gemm_grouped_native"):
+            f = getattr(L, name)
+            f.restype = i32
+            f.argtypes = [i32, i32, i32, ctypes.POINTER(GemmDesc), i32, vp]
         L.puro_status_string.restype = ctypes.c_char_p
         L.puro_status_string.argtypes = [i32]
         L.puro_fp8_version.restype = i32
@@ -523,12 +526,16 @@ def gemm_descs(layout, problems, bgran="128x128", out_dtype=torch.bfloat16):
 
 
 @_stream_allocs
-def puro_fp8_gemm_grouped(layout, problems, bgran="128x128", out_dtype=torch.bfloat16, stream=None):
+def puro_fp8_gemm_grouped(layout, problems, bgran="128x128", out_dtype=torch.bfloat16, stream=None, mx=False,
+                          native=False):
     """Independent blockwise-scaled E4M3 GEMMs sharing layout, B-scale
     granularity and output dtype, in as few launches as possible.
-    problems: list of (A, sA, B, sB) or (A, sA, B, sB, C); returns the list of C."""
+    problems: list of (A, sA, B, sB) or (A, sA, B, sB, C); returns the list of C.
+    mx=True calls puro_fp8_gemm_grouped_mx, native=True puro_fp8_gemm_grouped_native."""
+    if mx and native:
+        raise ValueError("mx and native are two different datapaths")
+    name = "puro_fp8_gemm_grouped_mx" if mx else "puro_fp8_gemm_grouped_native" if native else "puro_fp8_gemm_grouped"
     descs, outs = gemm_descs(layout, problems, bgran, out_dtype)
-    _check(lib().puro_fp8_gemm_grouped(LAYOUTS[layout], BGRAN[bgran],
-                                       PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32,
-                                       descs, len(problems), _stream(stream)), "puro_fp8_gemm_grouped")
+    _check(getattr(lib(), name)(LAYOUTS[layout], BGRAN[bgran], PURO_BF16 if out_dtype == torch.bfloat16 else PURO_F32,
+                                descs, len(problems), _stream(stream)), name)
     return outs

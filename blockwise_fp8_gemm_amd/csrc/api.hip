@@ -522,8 +522,11 @@ puro_status_t puro_fp8_gemm_native(puro_layout_t layout, int64_t M, int64_t N, i
     }
 }
 
-puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
-                                    const puro_gemm_desc_t *problems, int count, hipStream_t stream)
+// Datapaths of the grouped launcher.
+enum GroupDp { GROUP_EXACT, GROUP_MX, GROUP_NATIVE };
+
+static puro_status_t gemm_grouped_impl(GroupDp dp, puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                       const puro_gemm_desc_t *problems, int count, hipStream_t stream)
 {
     try {
         if (count < 0 || count > 4096)
@@ -546,6 +549,10 @@ puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, p
                                                     bgran, d.C, cdt, d.ldc);
                 if (st != PURO_OK)
                     return st;
+                // the FP8-matrix-core datapaths take aligned, non-empty products only
+                if (dp != GROUP_EXACT && d.M > 0 && d.N > 0 &&
+                    (!mx_aligned(d.M, d.N, g.K) || g.lda >= ((int64_t)1 << 28) || g.ldb >= ((int64_t)1 << 28)))
+                    return PURO_ERR_SHAPE;
                 p.seg[j] = puro::GemmSegment{g.K, g.A, g.lda, g.sA, g.B, g.ldb, g.sB};
             }
             p.nseg = d.nseg;
@@ -560,10 +567,32 @@ puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, p
             return PURO_ERR_ENUM;
         if (ps.empty())
             return PURO_OK;
-        return from_hip(puro::launch_gemm_group(ps.data(), (int)ps.size(), stream));
+        switch (dp) {
+        case GROUP_MX: return from_hip(puro::launch_gemm_group_mx(ps.data(), (int)ps.size(), stream));
+        case GROUP_NATIVE: return from_hip(puro::launch_gemm_group_native(ps.data(), (int)ps.size(), stream));
+        default: return from_hip(puro::launch_gemm_group(ps.data(), (int)ps.size(), stream));
+        }
     } catch (...) {
         return PURO_ERR_INTERNAL;
     }
+}
+
+puro_status_t puro_fp8_gemm_grouped(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                    const puro_gemm_desc_t *problems, int count, hipStream_t stream)
+{
+    return gemm_grouped_impl(GROUP_EXACT, layout, bgran, cdt, problems, count, stream);
+}
+
+puro_status_t puro_fp8_gemm_grouped_mx(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                       const puro_gemm_desc_t *problems, int count, hipStream_t stream)
+{
+    return gemm_grouped_impl(GROUP_MX, layout, bgran, cdt, problems, count, stream);
+}
+
+puro_status_t puro_fp8_gemm_grouped_native(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                           const puro_gemm_desc_t *problems, int count, hipStream_t stream)
+{
+    return gemm_grouped_impl(GROUP_NATIVE, layout, bgran, cdt, problems, count, stream);
 }
 
 const char *puro_status_string(puro_status_t status)

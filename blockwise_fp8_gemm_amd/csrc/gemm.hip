@@ -1286,7 +1286,7 @@ GemmArgs make_args(const GemmProblem &p)
 
 // One or more grouped launches of problems sharing a tile size: T = 128 or
 // 256 (fast_tile's two configurations).
-template <int T, int LAYOUT, int BGRAN, bool CBF16>
+template <int T, int LAYOUT, int BGRAN, bool CBF16, int DP>
 hipError_t launch_group_tiles(const std::vector<GemmArgs> &ps, hipStream_t st)
 {
     for (size_t lo = 0; lo < ps.size(); lo += kGroupMax) {
@@ -1319,15 +1319,15 @@ hipError_t launch_group_tiles(const std::vector<GemmArgs> &ps, hipStream_t st)
             // tile has no registers to spare for the segment lookup
             if (multi)
                 return hipErrorInvalidValue;
-            hipLaunchKernelGGL((gemm_group_kernel<CfgL, LAYOUT, BGRAN, CBF16, false>), grid, dim3(CfgL::THREADS), 0,
-                               st, g);
+            hipLaunchKernelGGL((gemm_group_kernel<CfgL, LAYOUT, BGRAN, CBF16, false, DP>), grid, dim3(CfgL::THREADS),
+                               0, st, g);
         } else {
             if (multi)
-                hipLaunchKernelGGL((gemm_group_kernel<CfgQ, LAYOUT, BGRAN, CBF16, true>), grid, dim3(CfgQ::THREADS), 0,
-                                   st, g);
+                hipLaunchKernelGGL((gemm_group_kernel<CfgQ, LAYOUT, BGRAN, CBF16, true, DP>), grid,
+                                   dim3(CfgQ::THREADS), 0, st, g);
             else
-                hipLaunchKernelGGL((gemm_group_kernel<CfgQ, LAYOUT, BGRAN, CBF16, false>), grid, dim3(CfgQ::THREADS),
-                                   0, st, g);
+                hipLaunchKernelGGL((gemm_group_kernel<CfgQ, LAYOUT, BGRAN, CBF16, false, DP>), grid,
+                                   dim3(CfgQ::THREADS), 0, st, g);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -1336,12 +1336,11 @@ hipError_t launch_group_tiles(const std::vector<GemmArgs> &ps, hipStream_t st)
     return hipSuccess;
 }
 
-// Estimated time of a group's problems on one tile configuration of the
-// FP32-exact datapath (the per-tile costs of fast_plan, work spread evenly
-// over the CUs).
-double group_estimate(const std::vector<GemmArgs> &ps, int cfg, bool bgran128)
+// Estimated time of a group's problems on one tile configuration of a
+// datapath (the per-tile costs of fast_plan, work spread evenly over the CUs).
+double group_estimate(const std::vector<GemmArgs> &ps, int cfg, int dp, bool bgran128)
 {
-    const TileCost c = tile_cost(cfg, DP_F16, bgran128);
+    const TileCost c = tile_cost(cfg, dp, bgran128);
     const int T = cfg == CFG_Q ? CfgQ::TM : CfgL::TM;
     double work = 0.0;
     for (const GemmArgs &x : ps) {
@@ -1355,12 +1354,14 @@ double group_estimate(const std::vector<GemmArgs> &ps, int cfg, bool bgran128)
     return work / kComputeUnits + c.launch;
 }
 
-template <int LAYOUT, int BGRAN, bool CBF16>
+template <int LAYOUT, int BGRAN, bool CBF16, int DP>
 hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
 {
     // Problems whose extents are multiples of 128 share grouped launches
-    // (longest K first, so that the longest tiles start first); any other
-    // non-empty problem runs on its own through the bounds-checked kernel.
+    // (longest K first, so that the longest tiles start first); on the
+    // FP32-exact datapath any other non-empty problem runs on its own through
+    // the bounds-checked kernel (the other datapaths admit aligned problems
+    // only: the API layer checks).
     std::vector<GemmArgs> fast;
     for (int i = 0; i < count; i++) {
         const GemmProblem &p = probs[i];
@@ -1371,6 +1372,8 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
             k_aligned = k_aligned && p.seg[j].K % 128 == 0;
         if (k_aligned && p.M % CfgQ::TM == 0 && p.N % CfgQ::TN == 0 && fast_ld_ok(make_args(p))) {
             fast.push_back(make_args(p));
+        } else if (DP != DP_F16) {
+            return hipErrorInvalidValue;
         } else {
             const GemmArgs a = make_args(p);
             const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
@@ -1391,39 +1394,55 @@ hipError_t launch_group_t(const GemmProblem *probs, int count, hipStream_t st)
     std::stable_sort(fast.begin(), fast.end(),
                      [&](const GemmArgs &x, const GemmArgs &y) { return blocks(x) > blocks(y); });
     std::vector<GemmArgs> large, small;
+    // 256 x 256 tiles: single-segment problems whose extents are multiples of
+    // 256 (on the FP32-exact datapath NT products only, its K-major fragments)
+    constexpr bool L_OK = DP != DP_F16 || LAYOUT == 0;
     for (const GemmArgs &x : fast) {
-        if (LAYOUT == 0 && x.nseg == 1 && x.M % CfgL::TM == 0 && x.N % CfgL::TN == 0) {
+        if (L_OK && x.nseg == 1 && x.M % CfgL::TM == 0 && x.N % CfgL::TN == 0) {
             large.push_back(x);
         } else {
             small.push_back(x);
         }
     }
     // the 256 x 256 tiles take the eligible problems when the estimate favours them
-    if (large.empty() || group_estimate(large, CFG_L, BGRAN == 1) >= group_estimate(large, CFG_Q, BGRAN == 1)) {
+    if (large.empty() ||
+        group_estimate(large, CFG_L, DP, BGRAN == 1) >= group_estimate(large, CFG_Q, DP, BGRAN == 1)) {
         small = fast;
         large.clear();
     }
-    if constexpr (LAYOUT == 0) {
+    if constexpr (L_OK) {
         if (!large.empty()) {
-            const hipError_t e = launch_group_tiles<256, LAYOUT, BGRAN, CBF16>(large, st);
+            const hipError_t e = launch_group_tiles<256, LAYOUT, BGRAN, CBF16, DP>(large, st);
             if (e != hipSuccess)
                 return e;
         }
     }
     if (small.empty())
         return hipSuccess;
-    return launch_group_tiles<128, LAYOUT, BGRAN, CBF16>(small, st);
+    return launch_group_tiles<128, LAYOUT, BGRAN, CBF16, DP>(small, st);
 }
 
-template <int LAYOUT>
+template <int LAYOUT, int DP>
 hipError_t launch_group_layout(const GemmProblem *probs, int count, hipStream_t st)
 {
     const GemmProblem &p = probs[0];
     if (p.bgran)
-        return p.c_bf16 ? launch_group_t<LAYOUT, 1, true>(probs, count, st)
-                        : launch_group_t<LAYOUT, 1, false>(probs, count, st);
-    return p.c_bf16 ? launch_group_t<LAYOUT, 0, true>(probs, count, st)
-                    : launch_group_t<LAYOUT, 0, false>(probs, count, st);
+        return p.c_bf16 ? launch_group_t<LAYOUT, 1, true, DP>(probs, count, st)
+                        : launch_group_t<LAYOUT, 1, false, DP>(probs, count, st);
+    return p.c_bf16 ? launch_group_t<LAYOUT, 0, true, DP>(probs, count, st)
+                    : launch_group_t<LAYOUT, 0, false, DP>(probs, count, st);
+}
+
+template <int DP>
+hipError_t launch_group_dp(const GemmProblem *probs, int count, hipStream_t st)
+{
+    if (count <= 0)
+        return hipSuccess;
+    switch (probs[0].layout) {
+    case 0: return launch_group_layout<0, DP>(probs, count, st);
+    case 1: return launch_group_layout<1, DP>(probs, count, st);
+    default: return launch_group_layout<2, DP>(probs, count, st);
+    }
 }
 
 size_t plan_workspace(const GemmProblem &p, int dp)
@@ -1490,13 +1509,17 @@ hipError_t launch_gemm_native(const GemmProblem &p, void *workspace, hipStream_t
 
 hipError_t launch_gemm_group(const GemmProblem *probs, int count, hipStream_t st)
 {
-    if (count <= 0)
-        return hipSuccess;
-    switch (probs[0].layout) {
-    case 0: return launch_group_layout<0>(probs, count, st);
-    case 1: return launch_group_layout<1>(probs, count, st);
-    default: return launch_group_layout<2>(probs, count, st);
-    }
+    return launch_group_dp<DP_F16>(probs, count, st);
+}
+
+hipError_t launch_gemm_group_mx(const GemmProblem *probs, int count, hipStream_t st)
+{
+    return launch_group_dp<DP_MX>(probs, count, st);
+}
+
+hipError_t launch_gemm_group_native(const GemmProblem *probs, int count, hipStream_t st)
+{
+    return launch_group_dp<DP_FP8>(probs, count, st);
 }
 
 } // namespace puro

@@ -86,5 +86,9 @@ hipError_t launch_gemm_native(const GemmProblem &p, void *workspace, hipStream_t
 // Independent problems sharing layout, B-scale granularity and output dtype;
 // needs no workspace.
 hipError_t launch_gemm_group(const GemmProblem *probs, int count, hipStream_t st);
+// The same on the scaled (MX) and on the native FP8 datapaths: aligned
+// problems only (M, N and every segment's K multiples of 128).
+hipError_t launch_gemm_group_mx(const GemmProblem *probs, int count, hipStream_t st);
+hipError_t launch_gemm_group_native(const GemmProblem *probs, int count, hipStream_t st);
 
 } // namespace puro

@@ -371,6 +371,25 @@ puro_status_t puro_fp8_gemm_native(puro_layout_t layout, int64_t M, int64_t N, i
                                    size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Grouped GEMMs on the two FP8-matrix-core datapaths: puro_fp8_gemm_grouped's
+ * arguments, descriptors, segment sums, accumulate-into outputs and
+ * validation, with every product computed as by puro_fp8_gemm_mx (power-of-two
+ * scales applied by the scaled MFMA) or by puro_fp8_gemm_native (amax / 448
+ * scales, FP8 block partials promoted in FP32), and with their precision.
+ * Passage: the setup paragraph of the model card (the main linear-layer GEMMs,
+ * backward ones included, in blockwise E4M3) and the DeepSeek-V3 design that
+ * the technical report's related-work paragraph cites; grouping is how one
+ * layer's seven weight gradients fill the GPU.
+ * Additionally, every non-empty problem needs M, N and each segment's K to be
+ * positive multiples of 128 and lda, ldb below 2^28 (else PURO_ERR_SHAPE,
+ * before anything is enqueued).  Needs no workspace.
+ */
+puro_status_t puro_fp8_gemm_grouped_mx(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                       const puro_gemm_desc_t *problems, int count, hipStream_t stream);
+puro_status_t puro_fp8_gemm_grouped_native(puro_layout_t layout, puro_bscale_t bgran, puro_dtype_t cdt,
+                                           const puro_gemm_desc_t *problems, int count, hipStream_t stream);
+
+/*
  * puro_fp8_gemm without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, validation, result and

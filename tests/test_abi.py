@@ -37,7 +37,7 @@ def test_header_declares_the_calls():
               "puro_fp8_quant_weight_grouped", "puro_fp8_quant_weight_grouped_pow2",
               "puro_fp8_swiglu_quant_dual", "puro_fp8_swiglu_quant_dual_pow2",
               "puro_fp8_gemm_native", "puro_fp8_gemm_native_workspace_size", "puro_fp8_gemm_noalloc",
-              "puro_fp8_version"):
+              "puro_fp8_gemm_grouped_mx", "puro_fp8_gemm_grouped_native", "puro_fp8_version"):
         assert n in names
 
 
@@ -189,10 +189,13 @@ def test_gemm_validation():
     assert _gemm(N=0, B=NUL, sB=NUL, C=NUL, ldb=256, ldc=0) == OK
 
 
-def _grouped(descs, count=None, layout=0, bg=1, cdt=1, arr=True):
+GROUPED = ["puro_fp8_gemm_grouped", "puro_fp8_gemm_grouped_mx", "puro_fp8_gemm_grouped_native"]
+
+
+def _grouped(descs, count=None, layout=0, bg=1, cdt=1, arr=True, name="puro_fp8_gemm_grouped"):
     n = len(descs)
     a = (pf.GemmDesc * max(n, 1))(*descs) if arr else None
-    return pf.lib().puro_fp8_gemm_grouped(layout, bg, cdt, a, n if count is None else count, None)
+    return getattr(pf.lib(), name)(layout, bg, cdt, a, n if count is None else count, None)
 
 
 def _desc(M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, C=P, ldc=256, nseg=1, acc=0, seg2=None):
@@ -201,25 +204,43 @@ def _desc(M=256, N=256, K=256, A=P, lda=256, sA=P, B=P, ldb=256, sB=P, C=P, ldc=
     return d
 
 
-def test_gemm_grouped_validation():
-    assert _grouped([]) == OK                                  # nothing to do
-    assert _grouped([], layout=5) == ENUM
-    assert _grouped([], cdt=3) == ENUM
-    assert _grouped([_desc()], count=-1) == SHAPE
-    assert _grouped([_desc()], count=4097) == SHAPE
-    assert _grouped([_desc()], arr=False, count=1) == NULL
-    assert _grouped([_desc()], bg=4) == ENUM
-    assert _grouped([_desc(), _desc(ldc=128)]) == SHAPE       # the second problem fails
-    assert _grouped([_desc(A=NUL), _desc()]) == NULL
-    assert _grouped([_desc(), _desc(C=P_ODD)]) == ALIGN
-    assert _grouped([_desc(), _desc(lda=264)]) == ALIGN
-    assert _grouped([_desc(nseg=0)]) == SHAPE
-    assert _grouped([_desc(nseg=5)]) == SHAPE
-    assert _grouped([_desc(acc=2)]) == ENUM
-    assert _grouped([_desc(seg2=(256, P, 128, P, P, 256, P))]) == SHAPE    # second segment's lda < K
-    assert _grouped([_desc(seg2=(256, NUL, 256, P, P, 256, P))]) == NULL
+@pytest.mark.parametrize("name", GROUPED)
+def test_gemm_grouped_validation(name):
+    def g(descs, **kw):
+        return _grouped(descs, name=name, **kw)
+    assert g([]) == OK                                  # nothing to do
+    assert g([], layout=5) == ENUM
+    assert g([], cdt=3) == ENUM
+    assert g([_desc()], count=-1) == SHAPE
+    assert g([_desc()], count=4097) == SHAPE
+    assert g([_desc()], arr=False, count=1) == NULL
+    assert g([_desc()], bg=4) == ENUM
+    assert g([_desc(), _desc(ldc=128)]) == SHAPE       # the second problem fails
+    assert g([_desc(A=NUL), _desc()]) == NULL
+    assert g([_desc(), _desc(C=P_ODD)]) == ALIGN
+    assert g([_desc(), _desc(lda=264)]) == ALIGN
+    assert g([_desc(nseg=0)]) == SHAPE
+    assert g([_desc(nseg=5)]) == SHAPE
+    assert g([_desc(acc=2)]) == ENUM
+    assert g([_desc(seg2=(256, P, 128, P, P, 256, P))]) == SHAPE    # second segment's lda < K
+    assert g([_desc(seg2=(256, NUL, 256, P, P, 256, P))]) == NULL
     # only empty problems: nothing enqueued
-    assert _grouped([_desc(M=0, A=NUL, sA=NUL, C=NUL), _desc(N=0, B=NUL, sB=NUL, C=NUL, ldc=0)]) == OK
+    assert g([_desc(M=0, A=NUL, sA=NUL, C=NUL), _desc(N=0, B=NUL, sB=NUL, C=NUL, ldc=0)]) == OK
+
+
+@pytest.mark.parametrize("name", GROUPED[1:])
+def test_gemm_grouped_fp8_datapaths_take_aligned_problems_only(name):
+    # each call holds a problem that the exact launcher would accept but these reject,
+    # so nothing is enqueued (the pointers are not device memory)
+    def g(descs):
+        return _grouped(descs, name=name)
+    assert g([_desc(), _desc(K=200)]) == SHAPE                        # K not a multiple of 128
+    assert g([_desc(M=192, C=P)]) == SHAPE                            # M
+    assert g([_desc(N=200, ldb=256, ldc=208)]) == SHAPE               # N
+    assert g([_desc(K=0)]) == SHAPE                                   # empty K with a non-empty output
+    assert g([_desc(seg2=(200, P, 256, P, P, 256, P))]) == SHAPE      # the second segment's K
+    big = 1 << 28
+    assert g([_desc(lda=big, K=256)]) == SHAPE                        # leading dimension beyond 2^28
 
 
 def test_workspace_size_is_defined_for_every_layout():
