@@ -310,3 +310,78 @@ def test_layer_adjacent_full_size(dev):
     for g, dW, hp in zip(gs, dWs, hprobs):
         seed += 1
         _check_sampled("NT", "1x128", hp, dW, T, seed, torch.float32)
+
+
+def _check_sampled_mc(layout, bgran, ops, C, K, seed, out):
+    """_check_sampled with the matrix-core bound of the native and MX datapaths:
+    2^-9 C_abs + (4 KB + 4) 2^-23 C_abs per entry (plus half a BF16 ulp), and a sampled
+    relative Frobenius error of at most 1e-3 for FP32 outputs."""
+    qa, sa, qb, sb = ops
+    M, N = C.shape
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, SAMPLES)
+    ns = rng.integers(0, N, SAMPLES)
+    ms[:4] = [0, 0, M - 1, M - 1]
+    ns[:4] = [0, N - 1, 0, N - 1]
+    ref = oracle.gemm_entries(layout, qa, sa, qb, sb, bgran, ms, ns)
+    ref_abs = oracle.gemm_entries(layout, qa & 0x7F, np.abs(sa), qb & 0x7F, np.abs(sb), bgran, ms, ns)
+    E = (2.0 ** -9 + (4 * ((K + 127) // 128) + 4) * 2.0 ** -23) * ref_abs
+    h = host(C)
+    got = bf16_to_f64(h[ms, ns]) if out == torch.bfloat16 else h[ms, ns].astype(np.float64)
+    tol = E + 2.0 ** -8 * (np.abs(ref) + E) if out == torch.bfloat16 else E
+    bad = np.flatnonzero(np.abs(got - ref) > tol)
+    assert bad.size == 0, ("entry", int(ms[bad[0]]), int(ns[bad[0]]), got[bad[0]], ref[bad[0]])
+    if out == torch.float32:
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 1e-3
+
+
+@pytest.mark.parametrize("dp", ["native", "mx"])
+def test_layer_grouped_fp8_datapaths_full_size(dev, dp):
+    """The benchmark's side steps at full size: the gate/up forward product and the layer's
+    seven weight gradients (K = 8,192) as grouped launches on the native-FP8 and on the MX
+    datapath (MX with the power-of-two quantisers), sampled against the oracle."""
+    T = synth.TOKENS
+    p2 = dp == "mx"
+    rule = {"rule": "pow2"} if p2 else {}
+    kw = {"mx": p2, "native": not p2}
+    shape = {g: (n, k, src) for g, n, k, src in synth.LAYER_GEMMS}
+    host_q, dev_q = {}, {}
+
+    def dual(name, x):
+        d = pf.puro_fp8_quant_dual(to_dev(x), True, pow2=p2)
+        r = oracle.quant_act(x, **rule) + oracle.quant_transpose(x, True, **rule)
+        torch.cuda.synchronize()
+        for t, ref, what in zip(d, r, ("q_row", "s_row", "q_tok", "s_tok")):
+            _same(t, ref, (name, what))
+        host_q[name], dev_q[name] = r, d
+
+    for i, (name, c) in enumerate(synth.LAYER_INPUTS):
+        dual(name, synth.normal((T, c), 1.0, synth.seed_of(4, 0, i), "bf16"))
+    for j, (g, n, k, src) in enumerate(synth.LAYER_GEMMS):
+        dual("dY_" + g, synth.normal((T, n), 1e-3, synth.seed_of(4, 0, 20 + j), "bf16"))
+    seed = 50
+    # forward gate and up on x_mlp, 128x128 weight scales
+    Ws = {g: synth.normal((shape[g][0], shape[g][1]), 0.02, synth.seed_of(4, 0, 15 + i))
+          for i, g in enumerate(("gate", "up"))}
+    for g in ("gate", "up"):
+        qw = pf.puro_fp8_quant_weight(to_dev(Ws[g]), pow2=p2)
+        rw = oracle.quant_weight(Ws[g], **rule)
+        torch.cuda.synchronize()
+        _same(qw[0], rw[0], ("qW", g))
+        _same(qw[1], rw[1], ("sW", g))
+        host_q["W_" + g], dev_q["W_" + g] = rw, qw
+    (hqx, hsx), (dqx, dsx) = host_q["x_mlp"][:2], dev_q["x_mlp"][:2]
+    Ys = pf.puro_fp8_gemm_grouped("NT", [(dqx, dsx) + dev_q["W_" + g] for g in ("gate", "up")],
+                                  out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    for g, Y in zip(("gate", "up"), Ys):
+        seed += 1
+        _check_sampled_mc("NT", "128x128", (hqx, hsx) + host_q["W_" + g], Y, shape[g][1], seed, torch.bfloat16)
+    gs = [g for g, _, _, _ in synth.LAYER_GEMMS]
+    dWs = pf.puro_fp8_gemm_grouped("NT", [dev_q["dY_" + g][2:] + dev_q[shape[g][2]][2:] for g in gs],
+                                   bgran="1x128", out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    for g, dW in zip(gs, dWs):
+        seed += 1
+        _check_sampled_mc("NT", "1x128", host_q["dY_" + g][2:] + host_q[shape[g][2]][2:], dW, T, seed,
+                          torch.float32)
