@@ -22,7 +22,9 @@ per layer.  Output: one JSON line (see the end of main()).  Besides the step,
 the gated activation fused into the dual quantiser (the down projection's
 input formed from the gate/up product), other GEMM forms and the whole step on
 the native-FP8 and scaled (MX) matrix-core variants are timed on their own and
-reported under "side_kernels"; none is part of the step or of its FLOP rate.
+reported under "side_kernels", as is the vendor library's plain BF16 GEMM on
+the layer's shapes (the stock rate of the FP16-class datapath the FP32-exact
+kernels run on); none is part of the step or of its FLOP rate.
 After the timing, the oracle leg (skipped with --no-cpu-baseline) checks the
 timed step's last layer -- every code and scale byte and sampled entries of
 its 15 GEMM outputs -- against the CPU oracle ("parity"), times the oracle on a
@@ -604,6 +606,55 @@ def gemm_side(pf, torch, dev, tokens, sp, reps):
     return out
 
 
+def vendor_bf16_side(torch, dev, tokens, reps):
+    """The same layer's 15 products (the forward and data-gradient GEMMs of the four fused
+    projections, the seven weight gradients) as plain BF16 GEMMs through torch.mm (the vendor
+    library), on E4M3-valued operands, BF16 out: no block scales, no widening, no promotion.
+    It runs on the same FP16-class matrix-core datapath as the FP32-exact kernels and gives the
+    rate a stock GEMM of that width reaches on these shapes on this GPU (context only)."""
+    import synth
+    T = tokens
+    probs = {"fwd": [(T, n, k) for _, n, k in synth.FUSED_GEMMS],
+             "dgrad": [(T, k, n) for _, n, k in synth.FUSED_GEMMS],
+             "wgrad": [(n, k, T) for _, n, k, _ in synth.LAYER_GEMMS]}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9301)
+
+    def e4m3_valued(r, c):
+        x = (torch.randn((r, c), device=dev, generator=gen) * 128.0).clamp_(-448.0, 448.0)
+        return x.to(torch.float8_e4m3fn).to(torch.bfloat16).contiguous()
+
+    out, tot_ms, tot_fl = {}, 0.0, 0.0
+    for kind, lst in probs.items():
+        k_ms, k_fl = 0.0, 0.0
+        for M, N, K in lst:
+            A, B = e4m3_valued(M, K), e4m3_valued(K, N)
+            C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                torch.mm(A, B, out=C)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = max(reps, 1) * 2
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(n):
+                torch.mm(A, B, out=C)
+            b.record()
+            torch.cuda.synchronize()
+            k_ms += a.elapsed_time(b) / n
+            k_fl += 2.0 * M * N * K
+            del A, B, C
+        out[kind] = round(k_fl / (k_ms * 1e-3) / 1e12, 1)
+        tot_ms += k_ms
+        tot_fl += k_fl
+    torch.cuda.empty_cache()
+    res = {"what": "torch.mm BF16 x BF16 -> BF16 on E4M3-valued operands, the layer's 15 products",
+           "ms_per_layer": round(tot_ms, 3), "TFLOP/s": round(tot_fl / (tot_ms * 1e-3) / 1e12, 1),
+           "TFLOP/s_by_kind": out}
+    log("  vendor BF16 GEMM on the layer's shapes (context, outside the step): %.3f ms/layer, %.0f TFLOP/s "
+        "(fwd %.0f, dgrad %.0f, wgrad %.0f)" % (tot_ms, res["TFLOP/s"], out["fwd"], out["dgrad"], out["wgrad"]))
+    return res
+
+
 def cpu_baseline(rows):
     """Time the oracle on a bounded sample of one layer of the same workload."""
     import numpy as np
@@ -892,6 +943,7 @@ def main():
     side = {"swiglu_quant_dual": swiglu_side(pf, torch, dev, tokens, sp, args.steps)}
     side.update(gemm_side(pf, torch, dev, tokens, sp, args.steps))
     side["steps"] = side_steps
+    side["vendor_bf16_gemm"] = vendor_bf16_side(torch, dev, tokens, args.steps)
     configs = measure_configs(pf, torch, dev, sp) if not args.no_configs else None
 
     dom_name, dom = max(per_name.items(), key=lambda kv: kv[1][0])
